@@ -1,0 +1,184 @@
+/*
+ * pa.h -- paged attention for AMD Instinct MI355X (gfx950).
+ *
+ * Attention computed straight out of a paged KV cache: keys and values live
+ * in a shared pool of fixed-size pages, every request owns an int32 page
+ * table that maps its logical pages to physical pages, and the kernels read
+ * the pages through that table while running online softmax, so neither a
+ * contiguous copy of the keys nor a score matrix is ever materialized.  This
+ * is the "Paged KV Cache" + "Paged FlashAttention" pair of the week-3
+ * material in the tiny-llm source reading (yangyang233333.github.io) and in
+ * "Build a vLLM from Scratch" (blog.mushroom.cv, Week 3).  Grouped-query
+ * attention and the causal mask are the week-1 items of the same source
+ * reading; split-K decode with a log-sum-exp merge is the Flash-Decoding item
+ * (adv04) of the mini-vllm-tutorial advanced-series design.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All array arguments are DEVICE pointers owned by the caller.  The library
+ *    never allocates or frees device memory and never synchronizes (except
+ *    pa_validate_metadata, which is a debugging aid).  All work is enqueued on
+ *    `stream` (a hipStream_t; NULL = the null stream) and the call returns as
+ *    soon as it is enqueued.
+ *  - Errors are return codes; nothing aborts or throws across the ABI.
+ *    PA_ERR_ARG: a null required pointer, a bad size or a misaligned pointer
+ *    (all arrays must be 16-byte aligned).  PA_ERR_UNSUPPORTED: a valid but
+ *    unimplemented shape (head_dim not 64/128, page_size not 16, fp32 prefill).
+ *    PA_ERR_WORKSPACE: workspace smaller than the plan needs.  PA_ERR_HIP: a
+ *    kernel launch failed.  PA_ERR_METADATA: pa_validate_metadata found a
+ *    contract violation in the device arrays.
+ *  - Layouts (row-major, contiguous):
+ *      q, out      [total_q, Hq, d]       rows ordered by request, then token
+ *      lse         float32 [total_q, Hq]  natural log of sum_j exp(scale*q.k_j)
+ *      k_pool,
+ *      v_pool      [num_pages, Hkv, P, d] one (page, KV head) block of P*d
+ *                                         elements is contiguous (4 KiB at
+ *                                         d = 128 in bf16)
+ *      page_table  int32 [B, max_pages_per_seq]
+ *      seq_lens    int32 [B]  keys held by request r, this step's included
+ *      q_offsets   int32 [B]  absolute position of request r's first query row
+ *    Request r owns n_r = seq_lens[r] - q_offsets[r] query rows; its row i
+ *    (position q_offsets[r] + i) sees keys 0 .. q_offsets[r] + i (causal).
+ *    Query head h reads KV head h / (Hq / Hkv).  Logical key j of request r is
+ *    slot j % P of physical page page_table[r][j / P].
+ *  - Device-array contract (checked only by pa_validate_metadata):
+ *    1 <= seq_lens[r] <= max_pages_per_seq * P, 0 <= q_offsets[r] < seq_lens[r],
+ *    sum_r n_r == total_q, and the first ceil(seq_lens[r] / P) entries of
+ *    row r are in [0, num_pages).  Page-table entries past that, page slots
+ *    past a request's last key, and unused pages may hold anything (-1, NaN):
+ *    the kernels never let them reach the output.
+ *  - bf16 is IEEE bfloat16; outputs are rounded to nearest even from float32
+ *    accumulators.  fp32 I/O is accepted by the decode, split and merge paths.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_ARG = 1,
+  PA_ERR_UNSUPPORTED = 2,
+  PA_ERR_WORKSPACE = 3,
+  PA_ERR_HIP = 4,
+  PA_ERR_METADATA = 5
+} pa_status;
+
+typedef enum pa_dtype { PA_BF16 = 0, PA_F32 = 1 } pa_dtype;
+
+/* Routes chosen by the dispatch guard. */
+typedef enum pa_path {
+  PA_PATH_DECODE = 0,        /* one workgroup per (request, KV head)           */
+  PA_PATH_DECODE_SPLIT = 1,  /* split-K partitions + log-sum-exp merge pass    */
+  PA_PATH_PREFILL = 2        /* query tiles through LDS-staged bf16 MFMA       */
+} pa_path;
+
+/* Host scalars describing one call; everything the planner needs without
+ * reading device memory. */
+typedef struct pa_desc {
+  int32_t num_seqs;          /* B: requests (rows of page_table/seq_lens/q_offsets) */
+  int32_t num_q_heads;       /* Hq                                                  */
+  int32_t num_kv_heads;      /* Hkv, divides Hq                                     */
+  int32_t head_dim;          /* d: 64 or 128                                        */
+  int32_t page_size;         /* P: 16                                               */
+  int32_t num_pages;         /* pages in each pool                                  */
+  int32_t max_pages_per_seq; /* row stride of page_table                            */
+  int32_t total_q;           /* rows of q/out/lse                                   */
+  int32_t max_seq_len;       /* host upper bound on seq_lens[r]                     */
+  int32_t max_q_len;         /* host upper bound on n_r (1 for decode)              */
+  int32_t dtype;             /* pa_dtype of q, the pools and out                    */
+} pa_desc;
+
+/* Output of the dispatch guard. */
+typedef struct pa_plan_info {
+  int32_t path;              /* pa_path                                             */
+  int32_t num_splits;        /* S: partitions per request (1 unless split)          */
+  int32_t grid_x;            /* workgroups the main kernel launches                 */
+  int32_t reserved;
+  uint64_t workspace_bytes;  /* bytes of scratch the route needs (0 if none)        */
+} pa_plan_info;
+
+/* Dispatch guard (pure host; reads no device memory).  Picks the route from
+ * the query length and the context length, as the attention dispatch guard
+ * of the tiny-llm source reading ("Prefill and decode need different
+ * kernels") does: max_q_len > 1 -> PA_PATH_PREFILL; otherwise decode, split
+ * into S partitions when B*Hkv workgroups would leave the chip's cu_count
+ * compute units under-filled and the contexts are long enough to split.
+ * cu_count <= 0 means "ask the current device" (falls back to 256). */
+pa_status pa_plan(const pa_desc* desc, int32_t cu_count, pa_plan_info* plan);
+
+/* Scratch bytes for split-K with num_splits partitions:
+ * B*Hq*S*d float32 partial outputs + B*Hq*S float32 partial lse, each
+ * 256-byte aligned.  Returns 0 for an invalid desc or num_splits < 1. */
+size_t pa_workspace_bytes(const pa_desc* desc, int32_t num_splits);
+
+/* Single-token decode: every request has exactly one query row (n_r = 1, so
+ * total_q == B and q_offsets[r] == seq_lens[r] - 1; q_offsets may be NULL).
+ * out [B, Hq, d] (dtype), lse float32 [B, Hq] (may be NULL).  The guard may
+ * route through split-K, which needs `workspace` of at least
+ * pa_plan(...).workspace_bytes bytes (else PA_ERR_WORKSPACE); workspace may be
+ * NULL when the plan needs none. */
+pa_status pa_decode(const pa_desc* desc, const void* q, const void* k_pool, const void* v_pool,
+                    const int32_t* page_table, const int32_t* seq_lens, const int32_t* q_offsets,
+                    float scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* Split-K decode with a caller-chosen partition count (Flash-Decoding):
+ * request r's ceil(seq_lens[r]/P) pages are cut into num_splits page-aligned
+ * ranges of ceil(pages_r / num_splits) pages (trailing ranges may be empty).
+ * Each (request, KV head, split) workgroup writes a normalized partial output
+ * and its lse into `workspace`; a merge pass combines them by the log-sum-exp
+ * rule and writes out and lse.  Same row contract as pa_decode.  Workspace
+ * layout: o_part float32 [B, Hq, S, d] at offset 0, lse_part float32
+ * [B, Hq, S] at the next 256-byte boundary; it holds the partials after the
+ * call.  num_splits in [1, 256]. */
+pa_status pa_split_merge(const pa_desc* desc, const void* q, const void* k_pool, const void* v_pool,
+                         const int32_t* page_table, const int32_t* seq_lens,
+                         const int32_t* q_offsets, float scale, int32_t num_splits,
+                         void* workspace, size_t workspace_bytes, void* out, float* lse,
+                         void* stream);
+
+/* Chunked prefill: request r's n_r query rows (a chunk of a prompt at prior
+ * offset q_offsets[r]) attend causally to keys 0 .. q_offsets[r] + i, all of
+ * them read from the pages (the chunk's own K/V already appended).  bf16
+ * only.  q_starts: int32 [B+1] exclusive prefix sum of n_r, or NULL to derive
+ * it on the device.  lse may be NULL. */
+pa_status pa_prefill_chunk(const pa_desc* desc, const void* q, const void* k_pool,
+                           const void* v_pool, const int32_t* page_table, const int32_t* seq_lens,
+                           const int32_t* q_offsets, const int32_t* q_starts, float scale,
+                           void* out, float* lse, void* stream);
+
+/* Log-sum-exp merge of split partials (the merge pass on its own; a test
+ * hook).  o_part float32 [rows, heads, S, d], lse_part float32 [rows, heads, S]
+ * (-inf marks an empty split) -> out [rows, heads, d] of out_dtype and
+ * lse float32 [rows, heads] (may be NULL). */
+pa_status pa_merge_partials(int32_t rows, int32_t heads, int32_t num_splits, int32_t head_dim,
+                            const float* o_part, const float* lse_part, void* out,
+                            int32_t out_dtype, float* lse, void* stream);
+
+/* Copy request `req`'s first seq_len keys out of the pools into contiguous
+ * k_out, v_out [seq_len, Hkv, d] (bit-exact; the page-table translation on
+ * its own, a test hook).  seq_len is a host value. */
+pa_status pa_gather_kv(const pa_desc* desc, const void* k_pool, const void* v_pool,
+                       const int32_t* page_table, int32_t req, int32_t seq_len, void* k_out,
+                       void* v_out, void* stream);
+
+/* Debugging aid: copies the metadata to the host (synchronizing `stream`)
+ * and checks the device-array contract above.  q_offsets may be NULL
+ * (decode).  Returns PA_OK or PA_ERR_METADATA. */
+pa_status pa_validate_metadata(const pa_desc* desc, const int32_t* page_table,
+                               const int32_t* seq_lens, const int32_t* q_offsets, void* stream);
+
+/* Static string naming a status code. */
+const char* pa_status_str(pa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,255 @@
+"""Paged attention on AMD MI355X: thin Python binding of libpa.so.
+
+Every function here has the name of the C entry point it wraps
+(include/pa.h) and does argument marshalling only: it checks tensor
+layouts, fills the host descriptor, allocates outputs with torch when the
+caller passes none, and calls the library on torch's current HIP stream.
+All attention work runs in the library's HIP kernels; there is no fallback.
+If libpa.so is missing the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpa.so")
+
+PA_OK, PA_ERR_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_METADATA = range(6)
+PA_BF16, PA_F32 = 0, 1
+PA_PATH_DECODE, PA_PATH_DECODE_SPLIT, PA_PATH_PREFILL = 0, 1, 2
+PATH_NAMES = {PA_PATH_DECODE: "decode", PA_PATH_DECODE_SPLIT: "decode_split",
+              PA_PATH_PREFILL: "prefill"}
+
+
+class PaError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {pa_status_str(code)}")
+
+
+class pa_desc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_seqs", "num_q_heads", "num_kv_heads", "head_dim", "page_size", "num_pages",
+        "max_pages_per_seq", "total_q", "max_seq_len", "max_q_len", "dtype")]
+
+
+class pa_plan_info(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("num_splits", ctypes.c_int32),
+                ("grid_x", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_uint64)]
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_D = ctypes.POINTER(pa_desc)
+_SIGS = {
+    "pa_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "pa_workspace_bytes": (ctypes.c_size_t, [_D, ctypes.c_int32]),
+    "pa_plan": (ctypes.c_int, [_D, ctypes.c_int32, ctypes.POINTER(pa_plan_info)]),
+    "pa_decode": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P,
+                                 ctypes.c_size_t, _P]),
+    "pa_split_merge": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_int32,
+                                      _P, ctypes.c_size_t, _P, _P, _P]),
+    "pa_prefill_chunk": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P,
+                                        _P]),
+    "pa_merge_partials": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_int32, _P, _P, _P, ctypes.c_int32, _P, _P]),
+    "pa_gather_kv": (ctypes.c_int, [_D, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]),
+    "pa_validate_metadata": (ctypes.c_int, [_D, _P, _P, _P, _P]),
+}
+EXPORTED = tuple(_SIGS)
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it first "
+                               "(python -m paged_kv_cache_02_amd.build or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def pa_status_str(code: int) -> str:
+    return lib().pa_status_str(int(code)).decode()
+
+
+def _check(code: int, where: str):
+    if code != PA_OK:
+        raise PaError(code, where)
+
+
+# ----------------------------------------------------------------------------
+# marshalling helpers
+# ----------------------------------------------------------------------------
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    if t.dtype == torch.float32:
+        return PA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def make_desc(q: torch.Tensor, k_pool: torch.Tensor, page_table: torch.Tensor,
+              seq_lens: torch.Tensor, max_seq_len: Optional[int] = None,
+              max_q_len: Optional[int] = None, q_offsets: Optional[torch.Tensor] = None) -> pa_desc:
+    """Host descriptor from tensor shapes; max_seq_len/max_q_len are read
+    from the device (a synchronization) only when not given."""
+    total_q, Hq, d = q.shape
+    NP, Hkv, P, d2 = k_pool.shape
+    if d2 != d:
+        raise ValueError("q and k_pool head_dim differ")
+    B, MP = page_table.shape
+    if max_seq_len is None:
+        max_seq_len = int(seq_lens.max().item()) if B else 0
+    if max_q_len is None:
+        if q_offsets is None:
+            max_q_len = 1 if B else 0
+        else:
+            max_q_len = int((seq_lens - q_offsets).max().item()) if B else 0
+    return pa_desc(B, Hq, Hkv, d, P, NP, MP, total_q, int(max_seq_len), int(max_q_len),
+                   _dtype_code(q))
+
+
+def _desc_dict(desc: pa_desc) -> dict:
+    return {n: getattr(desc, n) for n, _ in pa_desc._fields_}
+
+
+# ----------------------------------------------------------------------------
+# entry points
+# ----------------------------------------------------------------------------
+def pa_plan(desc: pa_desc, cu_count: int = 0) -> dict:
+    info = pa_plan_info()
+    _check(lib().pa_plan(ctypes.byref(desc), int(cu_count), ctypes.byref(info)), "pa_plan")
+    return {"path": PATH_NAMES[info.path], "num_splits": info.num_splits, "grid_x": info.grid_x,
+            "workspace_bytes": int(info.workspace_bytes)}
+
+
+def pa_workspace_bytes(desc: pa_desc, num_splits: int) -> int:
+    return int(lib().pa_workspace_bytes(ctypes.byref(desc), int(num_splits)))
+
+
+def _alloc_out(q, out, lse, want_lse=True):
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=q.device)
+    return out, lse
+
+
+def pa_decode(q, k_pool, v_pool, page_table, seq_lens, q_offsets, scale, *,
+              max_seq_len=None, out=None, lse=None, workspace=None, desc=None):
+    """Single-token decode; returns (out, lse)."""
+    desc = desc or make_desc(q, k_pool, page_table, seq_lens, max_seq_len)
+    out, lse = _alloc_out(q, out, lse)
+    plan = pa_plan(desc)
+    if workspace is None and plan["workspace_bytes"]:
+        workspace = torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().pa_decode(ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                           _ptr(page_table), _ptr(seq_lens), _ptr(q_offsets), float(scale),
+                           _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(q.device)),
+           "pa_decode")
+    return out, lse
+
+
+def pa_split_merge(q, k_pool, v_pool, page_table, seq_lens, q_offsets, scale, num_splits, *,
+                   max_seq_len=None, out=None, lse=None, workspace=None, desc=None):
+    """Split-K decode with num_splits partitions; returns (out, lse, workspace)
+    (the workspace holds the partials after the call)."""
+    desc = desc or make_desc(q, k_pool, page_table, seq_lens, max_seq_len)
+    out, lse = _alloc_out(q, out, lse)
+    need = pa_workspace_bytes(desc, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().pa_split_merge(ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                _ptr(page_table), _ptr(seq_lens), _ptr(q_offsets), float(scale),
+                                int(num_splits), _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse),
+                                _stream(q.device)), "pa_split_merge")
+    return out, lse, workspace
+
+
+def split_partials_view(desc: pa_desc, workspace: torch.Tensor, num_splits: int):
+    """(o_part [B,Hq,S,d], lse_part [B,Hq,S]) float32 views of a split workspace."""
+    B, Hq, d, S = desc.num_seqs, desc.num_q_heads, desc.head_dim, num_splits
+    o_bytes = (B * Hq * S * d * 4 + 255) // 256 * 256
+    f = workspace.view(torch.uint8)
+    o = f[:B * Hq * S * d * 4].view(torch.float32).view(B, Hq, S, d)
+    l = f[o_bytes:o_bytes + B * Hq * S * 4].view(torch.float32).view(B, Hq, S)
+    return o, l
+
+
+def pa_prefill_chunk(q, k_pool, v_pool, page_table, seq_lens, q_offsets, scale, *,
+                     q_starts=None, max_seq_len=None, max_q_len=None, out=None, lse=None,
+                     desc=None):
+    """Chunked prefill; returns (out, lse)."""
+    desc = desc or make_desc(q, k_pool, page_table, seq_lens, max_seq_len, max_q_len, q_offsets)
+    out, lse = _alloc_out(q, out, lse)
+    _check(lib().pa_prefill_chunk(ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                  _ptr(page_table), _ptr(seq_lens), _ptr(q_offsets),
+                                  _ptr(q_starts), float(scale), _ptr(out), _ptr(lse),
+                                  _stream(q.device)), "pa_prefill_chunk")
+    return out, lse
+
+
+def pa_merge_partials(o_part, lse_part, out_dtype=torch.bfloat16, *, out=None, lse=None):
+    """Merge o_part [rows, heads, S, d] / lse_part [rows, heads, S]; returns (out, lse)."""
+    rows, heads, S, d = o_part.shape
+    if out is None:
+        out = torch.empty(rows, heads, d, dtype=out_dtype, device=o_part.device)
+    if lse is None:
+        lse = torch.empty(rows, heads, dtype=torch.float32, device=o_part.device)
+    _check(lib().pa_merge_partials(rows, heads, S, d, _ptr(o_part), _ptr(lse_part), _ptr(out),
+                                   _dtype_code(out), _ptr(lse), _stream(o_part.device)),
+           "pa_merge_partials")
+    return out, lse
+
+
+def pa_gather_kv(k_pool, v_pool, page_table, req, seq_len, *, desc=None, seq_lens=None):
+    """Contiguous copies [seq_len, Hkv, d] of request req's keys and values."""
+    NP, Hkv, P, d = k_pool.shape
+    if desc is None:
+        B, MP = page_table.shape
+        desc = pa_desc(B, Hkv, Hkv, d, P, NP, MP, B, int(seq_len), 1, _dtype_code(k_pool))
+    k_out = torch.empty(seq_len, Hkv, d, dtype=k_pool.dtype, device=k_pool.device)
+    v_out = torch.empty_like(k_out)
+    _check(lib().pa_gather_kv(ctypes.byref(desc), _ptr(k_pool), _ptr(v_pool), _ptr(page_table),
+                              int(req), int(seq_len), _ptr(k_out), _ptr(v_out),
+                              _stream(k_pool.device)), "pa_gather_kv")
+    return k_out, v_out
+
+
+def pa_validate_metadata(desc: pa_desc, page_table, seq_lens, q_offsets=None) -> int:
+    """Returns the status code (PA_OK or PA_ERR_METADATA); synchronizes."""
+    return int(lib().pa_validate_metadata(ctypes.byref(desc), _ptr(page_table), _ptr(seq_lens),
+                                          _ptr(q_offsets), _stream(page_table.device)))
+
+
+__all__ = ["pa_desc", "pa_plan_info", "PaError", "lib", "make_desc", "pa_plan",
+           "pa_workspace_bytes", "pa_decode", "pa_split_merge", "pa_prefill_chunk",
+           "pa_merge_partials", "pa_gather_kv", "pa_validate_metadata", "pa_status_str",
+           "split_partials_view", "EXPORTED"]

@@ -1,0 +1,367 @@
+// C-ABI entry points of the paged-attention library: argument checks, the
+// dispatch guard, workspace carving and kernel launches on the caller's
+// stream.  See include/pa.h for the contract of every function.
+#include "pa.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <atomic>
+#include <vector>
+
+#include "pa_internal.h"
+
+namespace {
+
+// --------------------------------------------------------------------------
+// dispatch-guard tuning constants
+// --------------------------------------------------------------------------
+// Split decode until the grid holds about this many workgroups per CU, so
+// that uneven context lengths still leave every CU busy to the end.
+constexpr int kTargetWgsPerCu = 8;
+// A split must keep at least this many pages (4 per wave), or its fixed
+// costs (q load, cross-wave merge, partial write) stop being small.
+constexpr int kMinPagesPerSplit = 16;
+constexpr int kMaxSplits = 64;
+constexpr int kMaxSplitsApi = 256;
+constexpr int kDefaultCuCount = 256;
+constexpr size_t kAlign = 256;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int elem_bytes(int dtype) { return dtype == PA_BF16 ? 2 : 4; }
+
+pa_status check_desc(const pa_desc* d) {
+  if (d == nullptr) return PA_ERR_ARG;
+  if (d->num_seqs < 0 || d->num_q_heads <= 0 || d->num_kv_heads <= 0 || d->head_dim <= 0 ||
+      d->page_size <= 0 || d->num_pages <= 0 || d->max_pages_per_seq <= 0 || d->total_q < 0 ||
+      d->max_seq_len < 0 || d->max_q_len < 0)
+    return PA_ERR_ARG;
+  if (d->num_q_heads % d->num_kv_heads != 0) return PA_ERR_ARG;
+  if (d->dtype != PA_BF16 && d->dtype != PA_F32) return PA_ERR_ARG;
+  if ((long long)d->max_seq_len > (long long)d->max_pages_per_seq * d->page_size) return PA_ERR_ARG;
+  if (d->max_q_len > d->max_seq_len) return PA_ERR_ARG;
+  if (d->head_dim != 64 && d->head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (d->page_size != pa::kPageSize) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+int device_cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return kDefaultCuCount;
+  }
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    n = kDefaultCuCount;
+  }
+  cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Checks shared by the three decode-row entry points.
+pa_status check_decode_call(const pa_desc* d, const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* page_table, const int32_t* seq_lens, float scale,
+                            const void* out, const float* lse) {
+  pa_status st = check_desc(d);
+  if (st != PA_OK) return st;
+  if (d->total_q != d->num_seqs || d->max_q_len > 1) return PA_ERR_ARG;
+  if (!pa::decode_group_supported(d->num_q_heads / d->num_kv_heads)) return PA_ERR_UNSUPPORTED;
+  if (d->num_seqs == 0) return PA_OK;
+  if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !out) return PA_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out) ||
+      !aligned4(page_table) || !aligned4(seq_lens) || (lse && !aligned4(lse)))
+    return PA_ERR_ARG;
+  if (out == q) return PA_ERR_ARG;
+  if (!(scale > 0.f) || !isfinite(scale)) return PA_ERR_ARG;
+  return PA_OK;
+}
+
+size_t partial_o_bytes(const pa_desc* d, int S) {
+  return align_up((size_t)d->num_seqs * d->num_q_heads * (size_t)S * d->head_dim * sizeof(float));
+}
+size_t partial_lse_bytes(const pa_desc* d, int S) {
+  return align_up((size_t)d->num_seqs * d->num_q_heads * (size_t)S * sizeof(float));
+}
+
+pa::DecodeArgs decode_args(const pa_desc* d, const void* q, const void* k_pool, const void* v_pool,
+                           const int32_t* page_table, const int32_t* seq_lens, float scale) {
+  pa::DecodeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.page_table = page_table;
+  a.seq_lens = seq_lens;
+  a.num_seqs = d->num_seqs;
+  a.num_q_heads = d->num_q_heads;
+  a.num_kv_heads = d->num_kv_heads;
+  a.max_pages_per_seq = d->max_pages_per_seq;
+  a.num_pages = d->num_pages;
+  a.num_splits = 1;
+  a.write_partials = 0;
+  a.scale_log2 = scale * kLog2e;
+  return a;
+}
+
+// Split launch + merge launch shared by pa_decode (guard-chosen S) and
+// pa_split_merge (caller-chosen S).
+pa_status run_split(const pa_desc* d, pa::DecodeArgs a, int S, void* workspace, void* out,
+                    float* lse, hipStream_t stream) {
+  float* o_part = reinterpret_cast<float*>(workspace);
+  float* lse_part = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + partial_o_bytes(d, S));
+  a.num_splits = S;
+  a.write_partials = 1;
+  a.o_part = o_part;
+  a.lse_part = lse_part;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  if (pa::launch_decode(a, d->dtype, d->head_dim, G, stream) != hipSuccess) return PA_ERR_HIP;
+  pa::MergeArgs m;
+  m.o_part = o_part;
+  m.lse_part = lse_part;
+  m.out = out;
+  m.lse = lse;
+  m.rows = d->num_seqs;
+  m.heads = d->num_q_heads;
+  m.num_splits = S;
+  if (pa::launch_merge(m, d->dtype, d->head_dim, stream) != hipSuccess) return PA_ERR_HIP;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_str(pa_status s) {
+  switch (s) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_ARG: return "PA_ERR_ARG: invalid argument";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: shape or dtype not built";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace too small";
+    case PA_ERR_HIP: return "PA_ERR_HIP: kernel launch failed";
+    case PA_ERR_METADATA: return "PA_ERR_METADATA: device metadata violates the contract";
+  }
+  return "unknown pa_status";
+}
+
+size_t pa_workspace_bytes(const pa_desc* d, int32_t num_splits) {
+  if (check_desc(d) != PA_OK || num_splits < 1) return 0;
+  return partial_o_bytes(d, num_splits) + partial_lse_bytes(d, num_splits);
+}
+
+pa_status pa_plan(const pa_desc* d, int32_t cu_count, pa_plan_info* plan) {
+  pa_status st = check_desc(d);
+  if (st != PA_OK) return st;
+  if (plan == nullptr) return PA_ERR_ARG;
+  memset(plan, 0, sizeof(*plan));
+  const int cus = cu_count > 0 ? cu_count : device_cu_count();
+  const int G = d->num_q_heads / d->num_kv_heads;
+  if (d->max_q_len > 1) {
+    // chunked prefill: query tiles of packed (token, head-in-group) rows
+    if (d->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+    const int rows = pa::prefill_tile_rows(d->head_dim);
+    const long long tiles = ((long long)d->max_q_len * G + rows - 1) / rows;
+    plan->path = PA_PATH_PREFILL;
+    plan->num_splits = 1;
+    plan->grid_x = (int32_t)(tiles * d->num_seqs * d->num_kv_heads);
+    plan->workspace_bytes = 0;
+    return PA_OK;
+  }
+  if (!pa::decode_group_supported(G)) return PA_ERR_UNSUPPORTED;
+  const long long units = (long long)d->num_seqs * d->num_kv_heads;
+  const int max_pages = (d->max_seq_len + d->page_size - 1) / d->page_size;
+  const long long target = (long long)kTargetWgsPerCu * cus;
+  int S = 1;
+  if (units > 0 && units < target) {
+    long long want = (target + units - 1) / units;
+    long long cap = max_pages / kMinPagesPerSplit;
+    if (want > cap) want = cap;
+    if (want > kMaxSplits) want = kMaxSplits;
+    S = want >= 2 ? (int)want : 1;
+  }
+  plan->path = S > 1 ? PA_PATH_DECODE_SPLIT : PA_PATH_DECODE;
+  plan->num_splits = S;
+  plan->grid_x = (int32_t)(units * S);
+  plan->workspace_bytes = S > 1 ? pa_workspace_bytes(d, S) : 0;
+  return PA_OK;
+}
+
+pa_status pa_decode(const pa_desc* d, const void* q, const void* k_pool, const void* v_pool,
+                    const int32_t* page_table, const int32_t* seq_lens, const int32_t* q_offsets,
+                    float scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  (void)q_offsets;  // decode rows sit at position seq_len - 1 by contract
+  pa_status st = check_decode_call(d, q, k_pool, v_pool, page_table, seq_lens, scale, out, lse);
+  if (st != PA_OK || d->num_seqs == 0) return st;
+  pa_plan_info plan;
+  st = pa_plan(d, 0, &plan);
+  if (st != PA_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  pa::DecodeArgs a = decode_args(d, q, k_pool, v_pool, page_table, seq_lens, scale);
+  if (plan.num_splits == 1) {
+    a.out = out;
+    a.lse = lse;
+    const int G = d->num_q_heads / d->num_kv_heads;
+    return pa::launch_decode(a, d->dtype, d->head_dim, G, s) == hipSuccess ? PA_OK : PA_ERR_HIP;
+  }
+  if (workspace == nullptr || workspace_bytes < plan.workspace_bytes || !aligned16(workspace))
+    return PA_ERR_WORKSPACE;
+  return run_split(d, a, plan.num_splits, workspace, out, lse, s);
+}
+
+pa_status pa_split_merge(const pa_desc* d, const void* q, const void* k_pool, const void* v_pool,
+                         const int32_t* page_table, const int32_t* seq_lens,
+                         const int32_t* q_offsets, float scale, int32_t num_splits,
+                         void* workspace, size_t workspace_bytes, void* out, float* lse,
+                         void* stream) {
+  (void)q_offsets;
+  pa_status st = check_decode_call(d, q, k_pool, v_pool, page_table, seq_lens, scale, out, lse);
+  if (st != PA_OK) return st;
+  if (num_splits < 1 || num_splits > kMaxSplitsApi) return PA_ERR_ARG;
+  if (d->num_seqs == 0) return PA_OK;
+  const size_t need = pa_workspace_bytes(d, num_splits);
+  if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return PA_ERR_WORKSPACE;
+  pa::DecodeArgs a = decode_args(d, q, k_pool, v_pool, page_table, seq_lens, scale);
+  return run_split(d, a, num_splits, workspace, out, lse, reinterpret_cast<hipStream_t>(stream));
+}
+
+pa_status pa_prefill_chunk(const pa_desc* d, const void* q, const void* k_pool,
+                           const void* v_pool, const int32_t* page_table, const int32_t* seq_lens,
+                           const int32_t* q_offsets, const int32_t* q_starts, float scale,
+                           void* out, float* lse, void* stream) {
+  pa_status st = check_desc(d);
+  if (st != PA_OK) return st;
+  if (d->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  if (G < 1 || G > 16 || (G & (G - 1)) != 0) return PA_ERR_UNSUPPORTED;
+  if (d->num_seqs == 0 || d->total_q == 0) return PA_OK;
+  if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !q_offsets || !out) return PA_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out) ||
+      !aligned4(page_table) || !aligned4(seq_lens) || !aligned4(q_offsets) ||
+      (q_starts && !aligned4(q_starts)) || (lse && !aligned4(lse)))
+    return PA_ERR_ARG;
+  if (out == q) return PA_ERR_ARG;
+  if (!(scale > 0.f) || !isfinite(scale)) return PA_ERR_ARG;
+  if (d->max_q_len < 1) return PA_ERR_ARG;
+  const int rows = pa::prefill_tile_rows(d->head_dim);
+  const long long tiles = ((long long)d->max_q_len * G + rows - 1) / rows;
+  pa::PrefillArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.page_table = page_table;
+  a.seq_lens = seq_lens;
+  a.q_offsets = q_offsets;
+  a.q_starts = q_starts;
+  a.out = out;
+  a.lse = lse;
+  a.num_seqs = d->num_seqs;
+  a.num_q_heads = d->num_q_heads;
+  a.num_kv_heads = d->num_kv_heads;
+  a.max_pages_per_seq = d->max_pages_per_seq;
+  a.num_pages = d->num_pages;
+  a.tiles_per_seq = (int32_t)tiles;
+  a.scale_log2 = scale * kLog2e;
+  const hipError_t e = pa::launch_prefill(a, d->head_dim, G, reinterpret_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) return PA_ERR_UNSUPPORTED;
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_merge_partials(int32_t rows, int32_t heads, int32_t num_splits, int32_t head_dim,
+                            const float* o_part, const float* lse_part, void* out,
+                            int32_t out_dtype, float* lse, void* stream) {
+  if (rows < 0 || heads <= 0 || num_splits < 1 || num_splits > kMaxSplitsApi) return PA_ERR_ARG;
+  if (out_dtype != PA_BF16 && out_dtype != PA_F32) return PA_ERR_ARG;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (rows == 0) return PA_OK;
+  if (!o_part || !lse_part || !out) return PA_ERR_ARG;
+  if (!aligned16(o_part) || !aligned4(lse_part) || !aligned16(out) || (lse && !aligned4(lse)))
+    return PA_ERR_ARG;
+  pa::MergeArgs m;
+  m.o_part = o_part;
+  m.lse_part = lse_part;
+  m.out = out;
+  m.lse = lse;
+  m.rows = rows;
+  m.heads = heads;
+  m.num_splits = num_splits;
+  return pa::launch_merge(m, out_dtype, head_dim, reinterpret_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? PA_OK
+             : PA_ERR_HIP;
+}
+
+pa_status pa_gather_kv(const pa_desc* d, const void* k_pool, const void* v_pool,
+                       const int32_t* page_table, int32_t req, int32_t seq_len, void* k_out,
+                       void* v_out, void* stream) {
+  pa_status st = check_desc(d);
+  if (st != PA_OK) return st;
+  if (req < 0 || req >= d->num_seqs || seq_len < 0 ||
+      (long long)seq_len > (long long)d->max_pages_per_seq * d->page_size)
+    return PA_ERR_ARG;
+  if (seq_len == 0) return PA_OK;
+  if (!k_pool || !v_pool || !page_table || !k_out || !v_out) return PA_ERR_ARG;
+  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_out) || !aligned16(v_out) ||
+      !aligned4(page_table))
+    return PA_ERR_ARG;
+  pa::GatherArgs a;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.page_row = page_table + (size_t)req * d->max_pages_per_seq;
+  a.k_out = k_out;
+  a.v_out = v_out;
+  a.seq_len = seq_len;
+  a.num_kv_heads = d->num_kv_heads;
+  a.head_dim = d->head_dim;
+  a.elem_bytes = elem_bytes(d->dtype);
+  a.num_pages = d->num_pages;
+  return pa::launch_gather(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK
+                                                                                     : PA_ERR_HIP;
+}
+
+pa_status pa_validate_metadata(const pa_desc* d, const int32_t* page_table,
+                               const int32_t* seq_lens, const int32_t* q_offsets, void* stream) {
+  pa_status st = check_desc(d);
+  if (st != PA_OK) return st;
+  const int B = d->num_seqs;
+  if (B == 0) return PA_OK;
+  if (!page_table || !seq_lens) return PA_ERR_ARG;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  std::vector<int32_t> pt((size_t)B * d->max_pages_per_seq), sl(B), qo(B);
+  if (hipMemcpyAsync(pt.data(), page_table, pt.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipMemcpyAsync(sl.data(), seq_lens, sl.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      (q_offsets &&
+       hipMemcpyAsync(qo.data(), q_offsets, qo.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess) ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return PA_ERR_HIP;
+  long long total_q = 0;
+  for (int r = 0; r < B; ++r) {
+    const int L = sl[r];
+    if (L < 1 || L > d->max_seq_len || (long long)L > (long long)d->max_pages_per_seq * d->page_size)
+      return PA_ERR_METADATA;
+    const int o = q_offsets ? qo[r] : L - 1;
+    if (o < 0 || o >= L || L - o > (d->max_q_len > 0 ? d->max_q_len : 1)) return PA_ERR_METADATA;
+    total_q += L - o;
+    const int np = (L + d->page_size - 1) / d->page_size;
+    for (int p = 0; p < np; ++p) {
+      const int32_t id = pt[(size_t)r * d->max_pages_per_seq + p];
+      if (id < 0 || id >= d->num_pages) return PA_ERR_METADATA;
+    }
+  }
+  if (total_q != d->total_q) return PA_ERR_METADATA;
+  return PA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,107 @@
+// Log-sum-exp merge of split-K partials (gfx950).
+//
+// Split s of a (row, head) carries a partial output O_s normalized by its own
+// softmax sum and lse_s = ln(sum of exp(score) over the split's keys).  The
+// full result is LSE = M + ln(sum_s exp(lse_s - M)) with M = max_s lse_s and
+// out = sum_s exp(lse_s - LSE) * O_s; an empty split (lse_s = -inf) has zero
+// weight.  This is the combine step of split-K long-context decode
+// (Flash-Decoding, adv04 in the mini-vllm-tutorial advanced-series design).
+//
+// One wave per (row, head): lanes read the S partial lse values (strided by
+// 64), reduce max and sum with wave shuffles, then each lane produces d/64 of
+// the output dims, reading the S partial rows coalesced.
+#include "pa_internal.h"
+
+#include <math.h>
+
+namespace pa {
+namespace {
+
+constexpr int kWavesPerBlock = 4;
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+template <typename T>
+__device__ __forceinline__ T cast_out(float x);
+template <>
+__device__ __forceinline__ __bf16 cast_out<__bf16>(float x) { return (__bf16)x; }
+template <>
+__device__ __forceinline__ float cast_out<float>(float x) { return x; }
+
+template <typename T, int D>
+__global__ void __launch_bounds__(64 * kWavesPerBlock) merge_kernel(MergeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const long long rh = (long long)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  const long long nrh = (long long)a.rows * a.heads;
+  if (rh >= nrh) return;
+  const int S = a.num_splits;
+  const float* lp = a.lse_part + rh * S;
+  const float* op = a.o_part + rh * S * D;
+
+  float M = -INFINITY;
+  for (int s = lane; s < S; s += 64) M = fmaxf(M, lp[s]);
+  M = wave_max(M);
+  const float Mb = (M == -INFINITY) ? 0.f : M;   // all splits empty: weights stay 0
+  float tot = 0.f;
+  for (int s = lane; s < S; s += 64) {
+    const float v = lp[s];
+    tot += (v == -INFINITY) ? 0.f : exp2f((v - Mb) * kLog2e);
+  }
+  tot = wave_sum(tot);
+  const bool empty = !(tot > 0.f);
+  const float LSE = empty ? -INFINITY : Mb + logf(tot);
+
+  constexpr int kPer = D / 64;
+  float acc[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) acc[i] = 0.f;
+  if (!empty) {
+    for (int s = 0; s < S; ++s) {
+      const float v = lp[s];
+      const float w = (v == -INFINITY) ? 0.f : exp2f((v - LSE) * kLog2e);
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) acc[i] = fmaf(w, op[(long long)s * D + lane + 64 * i], acc[i]);
+    }
+  }
+  T* out = reinterpret_cast<T*>(a.out) + rh * D;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) out[lane + 64 * i] = cast_out<T>(acc[i]);
+  if (a.lse != nullptr && lane == 0) a.lse[rh] = LSE;
+}
+
+template <typename T, int D>
+hipError_t launch_t(const MergeArgs& a, hipStream_t s) {
+  const long long nrh = (long long)a.rows * a.heads;
+  if (nrh <= 0) return hipSuccess;
+  const long long grid = (nrh + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((merge_kernel<T, D>), dim3((unsigned)grid), dim3(64 * kWavesPerBlock), 0, s,
+                     a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_merge(const MergeArgs& a, int out_dtype, int head_dim, hipStream_t s) {
+  if (out_dtype == 0) {
+    if (head_dim == 128) return launch_t<__bf16, 128>(a, s);
+    if (head_dim == 64) return launch_t<__bf16, 64>(a, s);
+  } else if (out_dtype == 1) {
+    if (head_dim == 128) return launch_t<float, 128>(a, s);
+    if (head_dim == 64) return launch_t<float, 64>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

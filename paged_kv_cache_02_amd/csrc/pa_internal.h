@@ -1,0 +1,90 @@
+// Internal declarations shared by the library's translation units: the
+// parameter blocks handed to each kernel family and their host launchers.
+// Nothing here is part of the C ABI (include/pa.h is).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace pa {
+
+constexpr int kPageSize = 16;  // keys per page (the only page size built)
+
+// ---------------------------------------------------------------------------
+// decode / split-K partition kernel
+// ---------------------------------------------------------------------------
+struct DecodeArgs {
+  const void* q;            // [B, Hq, d]
+  const void* k_pool;       // [NP, Hkv, P, d]
+  const void* v_pool;
+  const int32_t* page_table;  // [B, MP]
+  const int32_t* seq_lens;    // [B]
+  void* out;                // [B, Hq, d]     (unsplit)
+  float* lse;               // [B, Hq] or null (unsplit)
+  float* o_part;            // [B, Hq, S, d]  (split)
+  float* lse_part;          // [B, Hq, S]     (split)
+  int32_t num_seqs, num_q_heads, num_kv_heads, max_pages_per_seq;
+  int32_t num_pages;        // pool size; page ids are clamped into [0, num_pages)
+  int32_t num_splits;       // S partitions per (request, KV head)
+  int32_t write_partials;   // 1: write o_part/lse_part; 0: write out/lse (needs S == 1)
+  float scale_log2;         // scale * log2(e)
+};
+
+// dtype: 0 = bf16, 1 = fp32.  Returns hipSuccess or the launch error.
+bool decode_group_supported(int group);
+hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int group, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// log-sum-exp merge of split partials
+// ---------------------------------------------------------------------------
+struct MergeArgs {
+  const float* o_part;      // [rows, heads, S, d]
+  const float* lse_part;    // [rows, heads, S]
+  void* out;                // [rows, heads, d]
+  float* lse;               // [rows, heads] or null
+  int32_t rows, heads, num_splits;
+};
+
+hipError_t launch_merge(const MergeArgs& a, int out_dtype, int head_dim, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// chunked prefill (bf16 MFMA)
+// ---------------------------------------------------------------------------
+struct PrefillArgs {
+  const void* q;            // [total_q, Hq, d] bf16
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  const int32_t* q_offsets;
+  const int32_t* q_starts;  // [B+1] or null (derived on the device)
+  void* out;                // [total_q, Hq, d] bf16
+  float* lse;               // [total_q, Hq] or null
+  int32_t num_seqs, num_q_heads, num_kv_heads, max_pages_per_seq;
+  int32_t num_pages;
+  int32_t tiles_per_seq;    // query tiles per (request, KV head) in the grid
+  float scale_log2;
+};
+
+// Rows of the packed (token, head-in-group) query tile one workgroup owns.
+int prefill_tile_rows(int head_dim);
+hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int group, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// page gather (test hook)
+// ---------------------------------------------------------------------------
+struct GatherArgs {
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* page_row;  // page_table + req * MP
+  void* k_out;              // [seq_len, Hkv, d]
+  void* v_out;
+  int32_t seq_len, num_kv_heads, head_dim, elem_bytes;
+  int32_t num_pages;        // page ids are clamped into [0, num_pages)
+};
+
+hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
+
+}  // namespace pa

@@ -1,0 +1,124 @@
+"""Host-side checks of the C-ABI library: it loads, exports every entry point
+include/pa.h declares, and its pure-host logic (the dispatch guard, workspace
+sizing, argument validation) behaves as documented.  No kernel is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_02_amd as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "pa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = header_functions()
+    assert set(names) == set(pa.EXPORTED), names
+    L = pa.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def desc(B=32, Hq=16, Hkv=8, d=128, P=16, NP=4096, MP=128, total_q=None, max_seq_len=2048,
+         max_q_len=1, dtype=pa.PA_BF16):
+    return pa.pa_desc(B, Hq, Hkv, d, P, NP, MP, B if total_q is None else total_q, max_seq_len,
+                      max_q_len, dtype)
+
+
+def test_status_strings():
+    for code in range(6):
+        assert pa.pa_status_str(code).startswith("PA_")
+
+
+def test_plan_routes_by_query_length():
+    info = pa.pa_plan(desc(max_q_len=512, total_q=2048), cu_count=256)
+    assert info["path"] == "prefill" and info["workspace_bytes"] == 0
+    info = pa.pa_plan(desc(), cu_count=256)
+    assert info["path"] in ("decode", "decode_split")
+
+
+def test_plan_splits_only_when_the_grid_is_small():
+    # 64 x 8 = 512 units at 8K context on 256 CUs -> split
+    d3 = desc(B=64, Hq=32, Hkv=8, NP=20000, MP=512, max_seq_len=8192)
+    p3 = pa.pa_plan(d3, cu_count=256)
+    assert p3["path"] == "decode_split" and p3["num_splits"] > 1
+    assert p3["workspace_bytes"] == pa.pa_workspace_bytes(d3, p3["num_splits"])
+    assert p3["grid_x"] == 64 * 8 * p3["num_splits"]
+    # plenty of units already -> no split
+    big = desc(B=1024, Hq=32, Hkv=8, NP=70000, MP=64, max_seq_len=1024)
+    assert pa.pa_plan(big, cu_count=256)["path"] == "decode"
+    # short contexts cannot be split below the minimum split length
+    short = desc(B=4, Hq=32, Hkv=8, MP=2, max_seq_len=32)
+    assert pa.pa_plan(short, cu_count=256)["num_splits"] == 1
+
+
+def test_workspace_bytes_formula():
+    d = desc(B=16, Hq=32, Hkv=8, d=64, NP=32768, MP=2048, max_seq_len=32768)
+    S = 16
+    o = 16 * 32 * S * 64 * 4
+    l = 16 * 32 * S * 4
+    align = lambda x: (x + 255) // 256 * 256
+    assert pa.pa_workspace_bytes(d, S) == align(o) + align(l)
+    assert pa.pa_workspace_bytes(d, 0) == 0
+
+
+@pytest.mark.parametrize("bad", [
+    dict(Hq=12, Hkv=8),            # Hq not a multiple of Hkv
+    dict(max_seq_len=5000, MP=128),  # longer than the page table can hold
+    dict(B=-1),
+    dict(dtype=7),
+])
+def test_plan_rejects_bad_descriptors(bad):
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_plan(desc(**bad), cu_count=256)
+    assert e.value.code == pa.PA_ERR_ARG
+
+
+@pytest.mark.parametrize("bad", [dict(d=96), dict(P=32)])
+def test_plan_reports_unbuilt_shapes(bad):
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_plan(desc(**bad), cu_count=256)
+    assert e.value.code == pa.PA_ERR_UNSUPPORTED
+
+
+def test_entry_points_reject_null_pointers_without_touching_the_device():
+    L = pa.lib()
+    d = desc()
+    rc = L.pa_decode(ctypes.byref(d), None, None, None, None, None, None, 0.1, None, None, None, 0,
+                     None)
+    assert rc == pa.PA_ERR_ARG
+    rc = L.pa_split_merge(ctypes.byref(d), None, None, None, None, None, None, 0.1, 4, None, 0,
+                          None, None, None)
+    assert rc == pa.PA_ERR_ARG
+    dp = desc(max_q_len=64, total_q=64)
+    rc = L.pa_prefill_chunk(ctypes.byref(dp), None, None, None, None, None, None, None, 0.1, None,
+                            None, None)
+    assert rc == pa.PA_ERR_ARG
+    rc = L.pa_merge_partials(4, 8, 2, 128, None, None, None, pa.PA_BF16, None, None)
+    assert rc == pa.PA_ERR_ARG
+    rc = L.pa_merge_partials(4, 8, 2, 96, None, None, None, pa.PA_BF16, None, None)
+    assert rc == pa.PA_ERR_UNSUPPORTED
+
+
+def test_decode_rejects_multi_row_requests():
+    L = pa.lib()
+    d = desc(max_q_len=4, total_q=128)
+    dummy = ctypes.c_void_p(256)
+    rc = L.pa_decode(ctypes.byref(d), dummy, dummy, dummy, dummy, dummy, None, 0.1, ctypes.c_void_p(512),
+                     None, None, 0, None)
+    assert rc == pa.PA_ERR_ARG
+
+
+def test_empty_batches_are_no_ops():
+    L = pa.lib()
+    d = desc(B=0, total_q=0)
+    rc = L.pa_decode(ctypes.byref(d), None, None, None, None, None, None, 0.1, None, None, None, 0,
+                     None)
+    assert rc == pa.PA_OK
