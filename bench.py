@@ -1,0 +1,262 @@
+"""Benchmark: one mixed continuous-batching step of paged attention on one GPU.
+
+A step is one pass of the whole hot path over one batch that is resident in
+HBM: the dispatch guard plans each route, pa_prefill_chunk runs the prefill
+chunks (bf16 MFMA) and pa_decode runs the decode rows (split-K + log-sum-exp
+merge when the guard picks it).  The workload is the mixed step with
+Qwen3-4B attention heads: 4 prefill chunks of 512 tokens at prior offsets
+0/512/1536/3072 plus 60 decode rows with contexts U[256, 4096]; 32 q heads,
+8 KV heads, d = 128, bf16, page size 16, permuted pool of 1.25x the pages.
+Inputs are synthetic N(0,1) (there are no weights or datasets here).
+
+Prints ONE JSON line.  `value` is the decode path's algorithmic KV GB/s; the
+prefill path's algorithmic TFLOP/s is reported beside it, and `roofline`
+describes whichever kernel takes the larger share of the step.  Two copies
+of the KV pool are used alternately so consecutive steps cannot be served
+from the 256 MB last-level cache.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+METRIC = "paged decode attn KV GB/s (% HBM peak); chunked-prefill TFLOP/s (% MFMA peak)"
+WORKLOAD = "mixed_step"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=15.0,
+                    help="wall-clock budget of the oracle's CPU baseline sample")
+    return ap.parse_args()
+
+
+def source_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "paged_kv_cache_02_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def decode_alg_bytes(b) -> int:
+    """K and V of every visible key once per KV head, q, out, lse, the page
+    table entries read and the two int32 metadata arrays."""
+    es = 2
+    keys = int(b.seq_lens.astype(np.int64).sum())
+    pages = int(((b.seq_lens.astype(np.int64) + b.page_size - 1) // b.page_size).sum())
+    B, Hq, d = b.num_seqs, b.num_q_heads, b.head_dim
+    return (keys * b.num_kv_heads * d * 2 * es + 2 * B * Hq * d * es + B * Hq * 4 + pages * 4
+            + 2 * B * 4)
+
+
+def prefill_alg_flops(b) -> int:
+    """4 * d * Hq per visible (query, key) pair: QK^T and PV, causal pairs only."""
+    n = (b.seq_lens - b.q_offsets).astype(np.int64)
+    o = b.q_offsets.astype(np.int64)
+    pairs = int((n * o + n * (n + 1) // 2).sum())
+    return 4 * b.head_dim * b.num_q_heads * pairs
+
+
+def load_traffic(kernel: str, src_hash: str):
+    """HBM bytes per launch measured with rocprofv3 counters for this kernel
+    source, or None if none were taken for the current source."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        with open(p) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != src_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(full, budget_s: float):
+    """The oracle, untuned, on a bounded sample of the same workload."""
+    import oracle as ORACLE
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    q, kp, vp = full.q_f32(), full.k_pool_f32(), full.v_pool_f32()
+    dec0, dec1 = full.notes["decode_requests"]
+    pf0, pf1 = full.notes["prefill_requests"]
+    # decode rows: as many as fit half the budget
+    t0 = time.perf_counter()
+    done, nbytes = 0, 0
+    for r in range(dec0, dec1):
+        ORACLE.paged_attention(q, kp, vp, full.page_table, full.seq_lens, full.q_offsets,
+                               full.scale, requests=[r])
+        done += 1
+        nbytes += int(full.seq_lens[r]) * full.num_kv_heads * full.head_dim * 2 * 2
+        if time.perf_counter() - t0 > budget_s / 2:
+            break
+    t_dec = time.perf_counter() - t0
+    # prefill: the first rows of the longest chunk
+    r = pf1 - 1
+    starts = full.q_row_starts
+    K, V = ORACLE.gather(kp, vp, full.page_table[r], int(full.seq_lens[r]))
+    pos = ORACLE.query_positions(int(full.seq_lens[r]), int(full.q_offsets[r]))
+    t1 = time.perf_counter()
+    rows, flops = 0, 0
+    step = 16
+    while time.perf_counter() - t1 < budget_s / 2 and rows < len(pos):
+        sl = slice(int(starts[r]) + rows, int(starts[r]) + rows + step)
+        ORACLE.attend(q[sl], K, V, pos[rows:rows + step], full.scale)
+        flops += int(sum(4 * full.head_dim * full.num_q_heads * (p + 1) for p in pos[rows:rows + step]))
+        rows += step
+    t_pf = time.perf_counter() - t1
+    return {
+        "value": round(nbytes / t_dec / 1e9, 3), "unit": "GB/s", "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done} of 60 decode rows ({nbytes / 1e6:.1f} MB of KV) in {t_dec:.1f} s; "
+                  f"prefill: {rows} rows of the 512-token chunk at offset 3072 in {t_pf:.1f} s",
+        "prefill_value": round(flops / t_pf / 1e12, 6), "prefill_unit": "TFLOP/s",
+        "host_cpus": os.cpu_count(),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this library has no multi-GPU path "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_02_amd as pa
+    import workloads as W
+
+    torch.cuda.init()
+    dev = torch.device("cuda:0")
+    full = W.make_config(WORKLOAD, seed=args.seed, poison=False)
+    pf = full.subset(*full.notes["prefill_requests"], name="prefill chunks")
+    dc = full.subset(*full.notes["decode_requests"], name="decode rows")
+
+    def to_dev(arr, dtype):
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16) \
+            if dtype == W.BF16 else torch.from_numpy(np.ascontiguousarray(arr))
+        return t.to(dev)
+
+    pools = [(to_dev(full.k_pool, full.dtype), to_dev(full.v_pool, full.dtype)) for _ in range(2)]
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+    pf_t = {"q": to_dev(pf.q, pf.dtype), "pt": i32(pf.page_table), "sl": i32(pf.seq_lens),
+            "qo": i32(pf.q_offsets), "qs": i32(pf.q_row_starts)}
+    dc_t = {"q": to_dev(dc.q, dc.dtype), "pt": i32(dc.page_table), "sl": i32(dc.seq_lens),
+            "qo": i32(dc.q_offsets)}
+    pf_desc = pa.make_desc(pf_t["q"], pools[0][0], pf_t["pt"], pf_t["sl"], pf.max_seq_len,
+                           pf.max_q_len)
+    dc_desc = pa.make_desc(dc_t["q"], pools[0][0], dc_t["pt"], dc_t["sl"], dc.max_seq_len, 1)
+    pf_plan = pa.pa_plan(pf_desc)
+    dc_plan = pa.pa_plan(dc_desc)
+    pf_out = torch.empty_like(pf_t["q"])
+    pf_lse = torch.empty(pf.total_q, pf.num_q_heads, dtype=torch.float32, device=dev)
+    dc_out = torch.empty_like(dc_t["q"])
+    dc_lse = torch.empty(dc.total_q, dc.num_q_heads, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(dc_plan["workspace_bytes"], 256), dtype=torch.uint8, device=dev)
+
+    def step(i, ev=None):
+        kp, vp = pools[i & 1]
+        if ev is not None:
+            ev[0].record()
+        pa.pa_prefill_chunk(pf_t["q"], kp, vp, pf_t["pt"], pf_t["sl"], pf_t["qo"], pf.scale,
+                            q_starts=pf_t["qs"], out=pf_out, lse=pf_lse, desc=pf_desc)
+        if ev is not None:
+            ev[1].record()
+        pa.pa_decode(dc_t["q"], kp, vp, dc_t["pt"], dc_t["sl"], dc_t["qo"], dc.scale,
+                     out=dc_out, lse=dc_lse, workspace=ws, desc=dc_desc)
+        if ev is not None:
+            ev[2].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps, events between the launches
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    pf_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    dc_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+
+    dec_bytes = decode_alg_bytes(dc)
+    pf_flops = prefill_alg_flops(pf)
+    dec_gbs = dec_bytes / (dc_ms * 1e-3) / 1e9
+    pf_tflops = pf_flops / (pf_ms * 1e-3) / 1e12
+
+    pf_hash = source_hash("prefill.hip")
+    dc_hash = source_hash("decode.hip", "merge.hip")
+    kernels = {
+        "prefill": {"bound": "mfma", "achieved": round(pf_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(pf_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "traffic": load_traffic("prefill", pf_hash), "ms": round(pf_ms, 4),
+                    "kernel": "prefill_kernel<128>", "work": pf_flops, "work_unit": "FLOP"},
+        "decode": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
+                   "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                   "traffic": load_traffic("decode", dc_hash), "ms": round(dc_ms, 4),
+                   "kernel": f"decode_kernel<bf16,128,4> x{dc_plan['num_splits']} splits + merge_kernel",
+                   "work": dec_bytes, "work_unit": "B"},
+    }
+    dominant = "prefill" if pf_ms >= dc_ms else "decode"
+    roof = {k: kernels[dominant][k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
+    roof["kernel"] = kernels[dominant]["kernel"]
+
+    result = {
+        "metric": METRIC,
+        "value": round(dec_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "mixed continuous-batching step, Qwen3-4B attention heads (32q/8kv, d=128)",
+            "prefill": "4 chunks x 512 tokens at offsets 0/512/1536/3072, causal",
+            "decode": "60 rows, contexts U[256,4096], seed %d" % full.seed,
+            "page_size": 16, "pool_pages": full.num_pages, "global_batch": 64,
+            "decode_plan": dc_plan, "prefill_plan": pf_plan,
+        },
+        "prefill_tflops": round(pf_tflops, 2),
+        "prefill_frac_of_mfma_peak": round(pf_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "decode_frac_of_hbm_peak": round(dec_gbs / HBM_PEAK_GBS, 4),
+        "kernels": kernels,
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(full, args.cpu_budget_s)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -46,10 +46,17 @@ def rne_bf16_f64(x: np.ndarray) -> np.ndarray:
     return W.bf16_bits_to_f32(W.f32_to_bf16_bits(x.astype(np.float32))).astype(np.float64)
 
 
+# Stress inputs (scores scaled far beyond N(0,1)) drive the output towards a
+# single value row, so |out| can exceed 2, where one bf16 rounding step of the
+# output alone is >= 2^-8 |out|.  Those tests add this relative term to the
+# absolute bar; the named workloads use the absolute bar alone.
+STRESS_REL = 2.0 ** -8
+
+
 def compare(b: W.PagedBatch, out: torch.Tensor, lse: torch.Tensor, ref_out, ref_lse, rows=None,
-            label=""):
+            label="", rel=0.0):
     """Element-wise comparison against the oracle; returns a stats dict and
-    asserts the tolerance for the batch's dtype."""
+    asserts the tolerance for the batch's dtype (|d out| <= tol + rel*|ref|)."""
     o = out_to_f64(out)
     l = lse.cpu().numpy().astype(np.float64)
     if rows is not None:
@@ -60,6 +67,7 @@ def compare(b: W.PagedBatch, out: torch.Tensor, lse: torch.Tensor, ref_out, ref_
     d_lse = np.abs(l - ref_lse)
     stats = {"max_abs_out_err": float(d_out.max()), "max_abs_lse_err": float(d_lse.max()),
              "max_abs_oracle_out": float(np.abs(ref_out).max())}
+    excess = float((d_out - rel * np.abs(ref_out)).max())
     if b.dtype == W.BF16:
         ulp = np.abs(o - rne_bf16_f64(ref_out))
         stats["max_abs_vs_rne_oracle"] = float(ulp.max())
@@ -67,6 +75,6 @@ def compare(b: W.PagedBatch, out: torch.Tensor, lse: torch.Tensor, ref_out, ref_
     else:
         tol_o, tol_l = OUT_TOL_F32, LSE_TOL_F32
     print(f"[{label}] {stats}", flush=True)
-    assert stats["max_abs_out_err"] <= tol_o, (label, stats)
+    assert excess <= tol_o, (label, stats)
     assert stats["max_abs_lse_err"] <= tol_l, (label, stats)
     return stats

@@ -9,7 +9,7 @@ import torch
 import oracle as ORACLE
 import paged_kv_cache_02_amd as pa
 import workloads as W
-from helpers import (LSE_TOL, OUT_TOL_BF16, compare, device_batch, oracle_run, out_to_f64,
+from helpers import (LSE_TOL, OUT_TOL_BF16, STRESS_REL, compare, device_batch, oracle_run, out_to_f64,
                      to_torch)
 
 pytestmark = pytest.mark.gpu
@@ -183,9 +183,9 @@ def test_large_scores_stay_finite():
     print("case large scores", flush=True)
     ro, rl = oracle_run(b)
     out, lse = run_decode(b)
-    compare(b, out, lse, ro, rl, label="scores x30")
+    compare(b, out, lse, ro, rl, label="scores x30", rel=STRESS_REL)
     out, lse, _ = run_split(b, 4)
-    compare(b, out, lse, ro, rl, label="scores x30 split")
+    compare(b, out, lse, ro, rl, label="scores x30 split", rel=STRESS_REL)
 
 
 def test_page_permutation_gives_bit_identical_output():

@@ -1,0 +1,123 @@
+"""GPU parity of the chunked-prefill path (bf16 MFMA) against the CPU oracle,
+through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_02_amd as pa
+import workloads as W
+from helpers import LSE_TOL, OUT_TOL_BF16, STRESS_REL, compare, device_batch, oracle_run, out_to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def run_prefill(b, dev=None, q_starts=None):
+    dev = dev or device_batch(b)
+    torch.cuda.synchronize()
+    out, lse = pa.pa_prefill_chunk(dev["q"], dev["k_pool"], dev["v_pool"], dev["page_table"],
+                                   dev["seq_lens"], dev["q_offsets"], b.scale, q_starts=q_starts,
+                                   max_seq_len=b.max_seq_len, max_q_len=b.max_q_len)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def chunk_batch(seed, seq_lens, q_offsets, Hq, Hkv, d, **kw):
+    return W.make_batch(f"chunks{seed}", seed, np.array(seq_lens, np.int32),
+                        np.array(q_offsets, np.int32), Hq, Hkv, d, 16, W.BF16, **kw)
+
+
+def test_mixed_step_prefill_chunks_full():
+    full = W.make_config("mixed_step")
+    b = full.subset(*full.notes["prefill_requests"], name="mixed prefill chunks")
+    print("case mixed_step prefill chunks 4x512 at offsets 0/512/1536/3072", flush=True)
+    out, lse = run_prefill(b)
+    ro, rl = oracle_run(b)
+    compare(b, out, lse, ro, rl, label="mixed-step prefill")
+
+
+@pytest.mark.parametrize("Hq,Hkv,d", [(32, 8, 128), (16, 8, 128), (8, 8, 128), (64, 8, 128),
+                                      (32, 8, 64), (4, 4, 64), (16, 1, 64)])
+def test_ragged_chunks(Hq, Hkv, d):
+    # chunk lengths not multiples of the 128-row tile, offsets not page-aligned,
+    # a one-token chunk, a chunk starting at 0 and a chunk spanning many pages
+    L = [45, 300, 1, 77, 1000, 130]
+    o = [0, 170, 0, 76, 357, 2]
+    b = chunk_batch(200 + Hq + d, L, o, Hq, Hkv, d)
+    print(f"case ragged chunks Hq={Hq} Hkv={Hkv} d={d}", flush=True)
+    out, lse = run_prefill(b)
+    ro, rl = oracle_run(b)
+    compare(b, out, lse, ro, rl, label=f"prefill G={Hq // Hkv} d={d}")
+
+
+def test_q_starts_given_or_derived_is_bit_identical():
+    b = chunk_batch(51, [100, 333, 64], [10, 200, 0], 32, 8, 128)
+    dev = device_batch(b)
+    out1, lse1 = run_prefill(b, dev)
+    qs = torch.from_numpy(b.q_row_starts.astype(np.int32)).cuda()
+    out2, lse2 = run_prefill(b, dev, q_starts=qs)
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+
+
+def test_page_permutation_gives_bit_identical_output():
+    b = chunk_batch(52, [700, 250], [300, 0], 32, 8, 128, pool_factor=2.0)
+    out1, lse1 = run_prefill(b)
+    rng = np.random.default_rng(9)
+    perm = rng.permutation(b.num_pages)
+    kp = np.empty_like(b.k_pool)
+    vp = np.empty_like(b.v_pool)
+    kp[perm] = b.k_pool
+    vp[perm] = b.v_pool
+    b.k_pool, b.v_pool = kp, vp
+    b.page_table = np.where(b.page_table >= 0, perm[np.maximum(b.page_table, 0)], -1).astype(np.int32)
+    out2, lse2 = run_prefill(b)
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+
+
+def test_last_row_matches_decode_of_that_position():
+    b = chunk_batch(53, [900], [500], 32, 8, 128)
+    out, lse = run_prefill(b)
+    dec = chunk_batch(53, [900], [899], 32, 8, 128)
+    # same pool, same page table; the decode query is the chunk's last row
+    dec.k_pool, dec.v_pool, dec.page_table = b.k_pool, b.v_pool, b.page_table
+    dec.q = b.q[-1:].copy()
+    dd = device_batch(dec)
+    out_d, lse_d = pa.pa_decode(dd["q"], dd["k_pool"], dd["v_pool"], dd["page_table"],
+                                dd["seq_lens"], dd["q_offsets"], dec.scale, max_seq_len=900)
+    torch.cuda.synchronize()
+    assert np.max(np.abs(out_to_f64(out[-1:]) - out_to_f64(out_d))) <= 2 * OUT_TOL_BF16
+    assert np.max(np.abs(lse[-1:].cpu().numpy() - lse_d.cpu().numpy())) <= LSE_TOL
+
+
+def test_large_scores_stay_finite():
+    b = chunk_batch(54, [400, 90], [100, 0], 32, 8, 128)
+    b.q = W.f32_to_bf16_bits(b.q_f32() * 30.0)
+    out, lse = run_prefill(b)
+    ro, rl = oracle_run(b)
+    compare(b, out, lse, ro, rl, label="prefill scores x30", rel=STRESS_REL)
+
+
+def test_zero_query_gives_running_mean():
+    b = chunk_batch(55, [77, 200], [0, 150], 8, 8, 128)
+    b.q[:] = 0
+    out, lse = run_prefill(b)
+    pos = np.concatenate([np.arange(0, 77), np.arange(150, 200)]).astype(np.float64)
+    assert np.max(np.abs(lse.cpu().numpy() - np.log(pos + 1)[:, None])) < LSE_TOL
+    ro, rl = oracle_run(b)
+    compare(b, out, lse, ro, rl, label="prefill q = 0")
+
+
+def test_nan_poison_does_not_leak():
+    b = chunk_batch(56, [33, 19, 250], [1, 0, 245], 32, 8, 128, pool_factor=3.0)
+    assert np.isnan(b.v_pool_f32()).any() and (b.page_table == -1).any()
+    out, lse = run_prefill(b)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    ro, rl = oracle_run(b)
+    compare(b, out, lse, ro, rl, label="prefill poisoned pool")
+
+
+def test_repeated_runs_are_bit_identical():
+    b = chunk_batch(57, [600, 1200], [88, 700], 32, 8, 128)
+    dev = device_batch(b)
+    o1, l1 = run_prefill(b, dev)
+    o2, l2 = run_prefill(b, dev)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
