@@ -74,76 +74,89 @@ __device__ __forceinline__ int swap12(int q) { return (q == 1) ? 2 : (q == 2 ? 1
 
 template <int D>
 struct Staging {
+  static_assert(D == 64 || D == 128, "staging layout is written for head_dim 64 or 128");
   static constexpr int kKChunks = kTileKeys * D / 8 / kThreads;  // 16-byte K chunks per thread
-  static constexpr int kVDimChunks = D / 8;                        // 8-dim chunks per key row
-  static constexpr int kVUnits = (kTileKeys / 4) * kVDimChunks;   // (key quad, dim chunk) units
-  static constexpr int kVPerThread = (kVUnits + kThreads - 1) / kThreads;
+  // V: thread (kq = lane % 16, c8 = lane / 16 + 4 * wave) holds keys 4kq..4kq+3
+  // of the tile at dims 8c8..8c8+7; threads with c8 >= D/8 stage nothing
   uint4 k[kKChunks];
-  uint4 v[kVPerThread][4];
+  uint4 v[4];
 };
 
-// Physical page ids of the 4 pages of KV tile kt, read once per tile as
-// workgroup-uniform values.  Pages past the ones the workgroup needs get -1.
-struct TilePages {
-  int id[kPagesPerTile];
+// Page ids.  At kernel start the workgroup copies the page-table entries
+// it needs (clamped into the pool) into LDS, so a tile's 4 page ids are LDS
+// broadcast reads (short, lgkmcnt-tracked) instead of global round trips.
+// A request whose needed pages exceed the LDS copy reads the page table
+// directly (a slower path with the same results).
+constexpr int kLdsPages = 2048;
+
+struct PageIds {
+  const int* lds;                  // LDS copy, or null
+  const int32_t* __restrict__ ptab;
+  int npages;                      // pages the workgroup needs
+  int num_pages;                   // pool size
 };
 
-__device__ __forceinline__ TilePages tile_pages(const int32_t* __restrict__ ptab, int kt,
-                                                int npages, int num_pages) {
-  TilePages tp;
-#pragma unroll
-  for (int m = 0; m < kPagesPerTile; ++m) {
-    const int lp = kt * kPagesPerTile + m;
-    int phys = -1;
-    if (lp < npages) {
-      phys = ptab[lp];
-      phys = phys < 0 ? 0 : (phys >= num_pages ? num_pages - 1 : phys);
-    }
-    tp.id[m] = __builtin_amdgcn_readfirstlane(phys);
+// Id of page m (uniform) of KV tile kt, or -1 past the needed pages.
+__device__ __forceinline__ int tile_page(const PageIds& pi, int kt, int m) {
+  const int lp = kt * kPagesPerTile + m;
+  if (lp >= pi.npages) return -1;
+  int id;
+  if (pi.lds != nullptr) {
+    id = pi.lds[lp];
+  } else {
+    id = pi.ptab[lp];
+    id = id < 0 ? 0 : (id >= pi.num_pages ? pi.num_pages - 1 : id);
   }
-  return tp;
+  return __builtin_amdgcn_readfirstlane(id);
 }
 
-// Global -> registers for one KV tile.  kb: first key of the tile; L: keys of
-// the request.  Every load is issued unconditionally from a valid address
-// (page 0 stands in for a missing page) and dead keys (>= L, or on a missing
-// page) are selected to zero afterwards, so the loads of a tile go out
-// back-to-back with no branch or wait between them.
+// Global -> registers for one KV tile kt (first key kb).  K: 16-byte chunk m
+// of thread tid is key m * (256 / (D/8)) + tid / (D/8) of the tile, so the
+// page of each load is uniform per wave; V: wave w stages page w (4 key
+// quads x D/8 dim chunks).  When the whole tile is live the loads are plain;
+// otherwise every load still comes from a valid address (page 0 stands in
+// for a missing page) and dead keys (>= L, or on a missing page) are
+// selected to zero.
 template <int D>
 __device__ __forceinline__ void stage_load(Staging<D>& st, const __bf16* __restrict__ kpool,
-                                           const __bf16* __restrict__ vpool, const TilePages& tp,
-                                           int kb, int L, int Hkv, int g, int tid) {
+                                           const __bf16* __restrict__ vpool, const PageIds& pi,
+                                           int kt, int L, int Hkv, int g, int tid, int wave) {
   const size_t blk = (size_t)kPageSize * D;
-  // K: chunk c = tid + 256 m -> key c / (D/8) of the tile, 16-byte chunk c % (D/8)
+  const int kb = kt * kTileKeys;
+  const int id0 = tile_page(pi, kt, 0);
+  const int id1 = tile_page(pi, kt, 1);
+  const int id2 = tile_page(pi, kt, 2);
+  const int last_id = tile_page(pi, kt, kPagesPerTile - 1);
+  const bool full = kb + kTileKeys <= L && last_id >= 0;
+  constexpr int kRowChunks = D / 8;                        // 16-byte chunks per key row
+  constexpr int kKeysPerPass = kThreads / kRowChunks;      // keys one pass of 256 threads covers
+  constexpr int kWavesPerPage = kPageSize / (64 / kRowChunks);
 #pragma unroll
   for (int m = 0; m < Staging<D>::kKChunks; ++m) {
-    const int c = tid + kThreads * m;
-    const int key = c / (D / 8);
-    const int ch = c % (D / 8);
-    const int pm = key / kPageSize;  // page within the tile (uniform when D/8 divides 256/16)
-    const int id = tp.id[0] * (pm == 0) + tp.id[1] * (pm == 1) + tp.id[2] * (pm == 2) + tp.id[3] * (pm == 3);
-    const bool live = id >= 0 && kb + key < L;
+    const int key = m * kKeysPerPass + tid / kRowChunks;   // key within the tile
+    const int pm = (m * kKeysPerPass) / kPageSize + wave / kWavesPerPage;  // uniform per wave
+    const int id = pm == 0 ? id0 : (pm == 1 ? id1 : (pm == 2 ? id2 : last_id));
     const int phys = id >= 0 ? id : 0;
-    const __bf16* src = kpool + ((size_t)phys * Hkv + g) * blk + (key % kPageSize) * D + ch * 8;
+    const __bf16* src = kpool + ((size_t)phys * Hkv + g) * blk + (key % kPageSize) * D +
+                        (tid % kRowChunks) * 8;
     const uint4 val = *reinterpret_cast<const uint4*>(src);
-    st.k[m] = live ? val : make_uint4(0, 0, 0, 0);
+    st.k[m] = (full || (id >= 0 && kb + key < L)) ? val : make_uint4(0, 0, 0, 0);
   }
-  // V: unit u = tid + 256 m -> key quad kq = u % 16, dim chunk c8 = u / 16
-#pragma unroll
-  for (int m = 0; m < Staging<D>::kVPerThread; ++m) {
-    const int u = tid + kThreads * m;
-    const int kq = u % (kTileKeys / 4);
-    const int c8 = (u / (kTileKeys / 4)) % (D / 8);
-    const int pm = kq / 4;
-    const int id = pm == 0 ? tp.id[0] : (pm == 1 ? tp.id[1] : (pm == 2 ? tp.id[2] : tp.id[3]));
+  {
+    const int lane = tid & 63;
+    const int kq = lane % 16;
+    const int c8raw = lane / 16 + 4 * wave;
+    const bool active = c8raw < D / 8;
+    const int c8 = active ? c8raw : 0;
+    const int pm = kq / 4;  // page of this key quad within the tile
+    const int id = pm == 0 ? id0 : (pm == 1 ? id1 : (pm == 2 ? id2 : last_id));
     const int phys = id >= 0 ? id : 0;
-    const __bf16* base = vpool + ((size_t)phys * Hkv + g) * blk + c8 * 8;
+    const __bf16* base = vpool + ((size_t)phys * Hkv + g) * blk + ((4 * kq) % kPageSize) * D + c8 * 8;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int slot = (4 * kq + j) % kPageSize;
-      const bool live = u < Staging<D>::kVUnits && id >= 0 && kb + 4 * kq + j < L;
-      const uint4 val = *reinterpret_cast<const uint4*>(base + slot * D);
-      st.v[m][j] = live ? val : make_uint4(0, 0, 0, 0);
+      const uint4 val = *reinterpret_cast<const uint4*>(base + j * D);
+      const int key = kb + 4 * kq + j;
+      st.v[j] = (full || (id >= 0 && key < L)) && active ? val : make_uint4(0, 0, 0, 0);
     }
   }
 }
@@ -153,34 +166,35 @@ __device__ __forceinline__ void stage_load(Staging<D>& st, const __bf16* __restr
 template <int D>
 __device__ __forceinline__ void stage_store(const Staging<D>& st, __bf16* kbuf, __bf16* vbuf,
                                             int tid) {
+  constexpr int kRowChunks = D / 8;
+  constexpr int kKeysPerPass = kThreads / kRowChunks;
 #pragma unroll
   for (int m = 0; m < Staging<D>::kKChunks; ++m) {
-    const int c = tid + kThreads * m;
-    const int key = c / (D / 8);
-    const int ch = c % (D / 8);
-    *reinterpret_cast<uint4*>(kbuf + key * Lds<D>::kKStride + ch * 8) = st.k[m];
+    const int key = m * kKeysPerPass + tid / kRowChunks;
+    *reinterpret_cast<uint4*>(kbuf + key * Lds<D>::kKStride + (tid % kRowChunks) * 8) = st.k[m];
   }
+  {
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int kq = lane % 16;             // key quad within the tile
+    const int c8 = lane / 16 + 4 * wave;  // 8-dim chunk
+    if (c8 < D / 8) {
+      const int col = 16 * (kq / 4) + 4 * swap12(kq % 4);
+      const uint32_t* k0 = reinterpret_cast<const uint32_t*>(&st.v[0]);
+      const uint32_t* k1 = reinterpret_cast<const uint32_t*>(&st.v[1]);
+      const uint32_t* k2 = reinterpret_cast<const uint32_t*>(&st.v[2]);
+      const uint32_t* k3 = reinterpret_cast<const uint32_t*>(&st.v[3]);
 #pragma unroll
-  for (int m = 0; m < Staging<D>::kVPerThread; ++m) {
-    const int u = tid + kThreads * m;
-    if (u >= Staging<D>::kVUnits) break;
-    const int kq = u % (kTileKeys / 4);
-    const int c8 = u / (kTileKeys / 4);
-    const int col = 16 * (kq / 4) + 4 * swap12(kq % 4);
-    const uint32_t* k0 = reinterpret_cast<const uint32_t*>(&st.v[m][0]);
-    const uint32_t* k1 = reinterpret_cast<const uint32_t*>(&st.v[m][1]);
-    const uint32_t* k2 = reinterpret_cast<const uint32_t*>(&st.v[m][2]);
-    const uint32_t* k3 = reinterpret_cast<const uint32_t*>(&st.v[m][3]);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {   // dword w holds dims 2w (low half) and 2w+1 (high half)
-      uint2 lo, hi;
-      lo.x = (k0[w] & 0xFFFFu) | (k1[w] << 16);
-      lo.y = (k2[w] & 0xFFFFu) | (k3[w] << 16);
-      hi.x = (k0[w] >> 16) | (k1[w] & 0xFFFF0000u);
-      hi.y = (k2[w] >> 16) | (k3[w] & 0xFFFF0000u);
-      const int d0 = c8 * 8 + 2 * w;
-      *reinterpret_cast<uint2*>(vbuf + d0 * Lds<D>::kVStride + col) = lo;
-      *reinterpret_cast<uint2*>(vbuf + (d0 + 1) * Lds<D>::kVStride + col) = hi;
+      for (int w = 0; w < 4; ++w) {   // dword w holds dims 2w (low half) and 2w+1 (high half)
+        uint2 lo, hi;
+        lo.x = (k0[w] & 0xFFFFu) | (k1[w] << 16);
+        lo.y = (k2[w] & 0xFFFFu) | (k3[w] << 16);
+        hi.x = (k0[w] >> 16) | (k1[w] & 0xFFFF0000u);
+        hi.y = (k2[w] >> 16) | (k3[w] & 0xFFFF0000u);
+        const int d0 = c8 * 8 + 2 * w;
+        *reinterpret_cast<uint2*>(vbuf + d0 * Lds<D>::kVStride + col) = lo;
+        *reinterpret_cast<uint2*>(vbuf + (d0 + 1) * Lds<D>::kVStride + col) = hi;
+      }
     }
   }
 }
@@ -268,54 +282,42 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
   float l_run = 0.f;
   const float sl2 = a.scale_log2;
 
-  Staging<D> stg;
-  TilePages tp = tile_pages(ptab, 0, npages_c, a.num_pages);
-  stage_load<D>(stg, kpool, vpool, tp, 0, L, Hkv, g, tid);
-  if (ntiles > 1) tp = tile_pages(ptab, 1, npages_c, a.num_pages);
-  stage_store<D>(stg, smem, smem + Lds<D>::kKElems, tid);
-  __syncthreads();
-
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int kb = kt * kTileKeys;
-    const bool more = kt + 1 < ntiles;
-    if (more) {
-      stage_load<D>(stg, kpool, vpool, tp, kb + kTileKeys, L, Hkv, g, tid);
-      if (kt + 2 < ntiles) tp = tile_pages(ptab, kt + 2, npages_c, a.num_pages);
-    }
-    const __bf16* kbuf = smem + (kt & 1) * Lds<D>::kBufElems;
+  // one KV tile: S^T, mask, online softmax, O^T += V^T P^T (reads LDS only)
+  auto compute_tile = [&](const __bf16* kbuf, int kb) {
     const __bf16* vbuf = kbuf + Lds<D>::kKElems;
-
     if (kb <= pos_hi) {  // some key of the tile is visible to some row of this wave
       // ---- S^T = K Q^T over two 32-key blocks ----
       floatx16_t sacc[2];
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[kb2][i] = 0.f;
         const __bf16* krow = kbuf + (kb2 * 32 + lrow) * Lds<D>::kKStride + 8 * half;
+        const floatx16_t zero = {};
+        sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            as_bf16x8(*reinterpret_cast<const uint4*>(krow)), as_bf16x8(qv[0]), zero, 0, 0, 0);
 #pragma unroll
-        for (int s = 0; s < kKSteps; ++s) {
+        for (int s = 1; s < kKSteps; ++s) {
           const uint4 kv = *reinterpret_cast<const uint4*>(krow + 16 * s);
           sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), as_bf16x8(qv[s]),
                                                               sacc[kb2], 0, 0, 0);
         }
       }
-      // ---- scale, causal mask, tile max ----
-      const bool masked = kb + kTileKeys - 1 > pos_lo;
+      // ---- causal mask (diagonal tiles only), tile max on raw scores ----
+      if (kb + kTileKeys - 1 > pos_lo) {
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = kb + kb2 * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+            sacc[kb2][i] = key <= pos ? sacc[kb2][i] : -INFINITY;
+          }
+      }
       float tmax = -INFINITY;
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
+      for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kb + kb2 * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-          float x = sacc[kb2][i] * sl2;
-          if (masked) x = key <= pos ? x : -INFINITY;
-          sacc[kb2][i] = x;
-          tmax = fmaxf(tmax, x);
-        }
-      }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      // ---- lazy online-softmax rescale ----
+        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[kb2][i]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * sl2;   // scale > 0 commutes with max
+      // ---- lazy online-softmax rescale (m_run is in scaled log2 units) ----
       const bool need = tmax > m_run + kRescaleLog2;
       if (__builtin_expect(__any(need), 0)) {
         const float mn = fmaxf(m_run, tmax);
@@ -327,17 +329,17 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
           for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
         m_run = mn;
       }
-      // ---- probabilities, packed to bf16 as the P^T operand ----
+      // ---- probabilities p = exp2(s * scale_log2 - m), packed to bf16 as P^T ----
+      // m_run is finite here: key 0 is visible to every row, so the first
+      // tile sets it; masked scores are -inf and exp2(-inf) = 0.
       uint32_t pk[2][8];
       float lsum = 0.f;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
-          const float x0 = sacc[kb2][i];
-          const float x1 = sacc[kb2][i + 1];
-          const float p0 = x0 == -INFINITY ? 0.f : fast_exp2(x0 - m_run);
-          const float p1 = x1 == -INFINITY ? 0.f : fast_exp2(x1 - m_run);
+          const float p0 = fast_exp2(fmaf(sacc[kb2][i], sl2, -m_run));
+          const float p1 = fast_exp2(fmaf(sacc[kb2][i + 1], sl2, -m_run));
           lsum += p0 + p1;
           pk[kb2][i / 2] = pack_bf16x2(p0, p1);
         }
@@ -362,9 +364,49 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
         }
       }
     }
-    if (more) stage_store<D>(stg, smem + ((kt + 1) & 1) * Lds<D>::kBufElems,
-                             smem + ((kt + 1) & 1) * Lds<D>::kBufElems + Lds<D>::kKElems, tid);
+  };
+
+  // Software pipeline over KV tiles, two tiles of loads in flight: while
+  // tile kt is computed out of one LDS buffer, tile kt+1 sits in one set of
+  // staging registers (loaded during the previous step) and tile kt+2 is
+  // being loaded into the other.  Prefetch loads past the last tile read a
+  // valid stand-in page and are never stored.  Unrolled by two so that the
+  // staging register sets and LDS buffers are indexed statically.
+  __shared__ int s_pages[kLdsPages];
+  PageIds pi;
+  pi.ptab = ptab;
+  pi.npages = npages_c;
+  pi.num_pages = a.num_pages;
+  pi.lds = nullptr;
+  if (npages_c <= kLdsPages) {
+    for (int i = tid; i < npages_c; i += kThreads) {
+      int id = ptab[i];
+      s_pages[i] = id < 0 ? 0 : (id >= a.num_pages ? a.num_pages - 1 : id);
+    }
+    pi.lds = s_pages;
     __syncthreads();
+  }
+  Staging<D> sA, sB;
+  stage_load<D>(sA, kpool, vpool, pi, 0, L, Hkv, g, tid, wave);
+  stage_load<D>(sB, kpool, vpool, pi, 1, L, Hkv, g, tid, wave);
+  __bf16* buf0 = smem;
+  __bf16* buf1 = smem + Lds<D>::kBufElems;
+  stage_store<D>(sA, buf0, buf0 + Lds<D>::kKElems, tid);
+  __syncthreads();
+
+  for (int kt = 0;;) {
+    // even step: tile kt in buf0, tile kt+1 in sB, tile kt+2 -> sA
+    stage_load<D>(sA, kpool, vpool, pi, kt + 2, L, Hkv, g, tid, wave);
+    compute_tile(buf0, kt * kTileKeys);
+    if (kt + 1 < ntiles) stage_store<D>(sB, buf1, buf1 + Lds<D>::kKElems, tid);
+    __syncthreads();
+    if (++kt >= ntiles) break;
+    // odd step: tile kt in buf1, tile kt+1 in sA, tile kt+2 -> sB
+    stage_load<D>(sB, kpool, vpool, pi, kt + 2, L, Hkv, g, tid, wave);
+    compute_tile(buf1, kt * kTileKeys);
+    if (kt + 1 < ntiles) stage_store<D>(sA, buf0, buf0 + Lds<D>::kKElems, tid);
+    __syncthreads();
+    if (++kt >= ntiles) break;
   }
 
   // ---- normalize and write ----
