@@ -147,11 +147,17 @@ pa_status pa_split_merge(const pa_desc* desc, const void* q, const void* k_pool,
  * offset q_offsets[r]) attend causally to keys 0 .. q_offsets[r] + i, all of
  * them read from the pages (the chunk's own K/V already appended).  bf16
  * only.  q_starts: int32 [B+1] exclusive prefix sum of n_r, or NULL to derive
- * it on the device.  lse may be NULL. */
+ * it on the device.  lse may be NULL.  When the grid is small against the
+ * chip, the guard splits long query tiles along their key range and merges
+ * the partials by log-sum-exp; that needs `workspace` of at least
+ * pa_plan(...).workspace_bytes bytes (PA_ERR_WORKSPACE if a smaller one is
+ * given).  workspace = NULL runs every tile unsplit (always valid, slower on
+ * unbalanced batches). */
 pa_status pa_prefill_chunk(const pa_desc* desc, const void* q, const void* k_pool,
                            const void* v_pool, const int32_t* page_table, const int32_t* seq_lens,
                            const int32_t* q_offsets, const int32_t* q_starts, float scale,
-                           void* out, float* lse, void* stream);
+                           void* out, float* lse, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /* Log-sum-exp merge of split partials (the merge pass on its own; a test
  * hook).  o_part float32 [rows, heads, S, d], lse_part float32 [rows, heads, S]

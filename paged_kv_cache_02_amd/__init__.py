@@ -56,7 +56,7 @@ _SIGS = {
     "pa_split_merge": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_int32,
                                       _P, ctypes.c_size_t, _P, _P, _P]),
     "pa_prefill_chunk": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P,
-                                        _P]),
+                                        _P, ctypes.c_size_t, _P]),
     "pa_merge_partials": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                          ctypes.c_int32, _P, _P, _P, ctypes.c_int32, _P, _P]),
     "pa_gather_kv": (ctypes.c_int, [_D, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]),
@@ -205,14 +205,21 @@ def split_partials_view(desc: pa_desc, workspace: torch.Tensor, num_splits: int)
 
 def pa_prefill_chunk(q, k_pool, v_pool, page_table, seq_lens, q_offsets, scale, *,
                      q_starts=None, max_seq_len=None, max_q_len=None, out=None, lse=None,
-                     desc=None):
-    """Chunked prefill; returns (out, lse)."""
+                     workspace=None, split=True, desc=None):
+    """Chunked prefill; returns (out, lse).  split=False runs without a
+    workspace (every query tile over its whole key range)."""
     desc = desc or make_desc(q, k_pool, page_table, seq_lens, max_seq_len, max_q_len, q_offsets)
     out, lse = _alloc_out(q, out, lse)
+    if split and workspace is None:
+        need = pa_plan(desc)["workspace_bytes"]
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().pa_prefill_chunk(ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool),
                                   _ptr(page_table), _ptr(seq_lens), _ptr(q_offsets),
                                   _ptr(q_starts), float(scale), _ptr(out), _ptr(lse),
-                                  _stream(q.device)), "pa_prefill_chunk")
+                                  _ptr(workspace), ws_bytes, _stream(q.device)),
+           "pa_prefill_chunk")
     return out, lse
 
 

@@ -24,6 +24,13 @@ constexpr int kTargetWgsPerCu = 8;
 // costs (q load, cross-wave merge, partial write) stop being small.
 constexpr int kMinPagesPerSplit = 16;
 constexpr int kMaxSplits = 64;
+// Prefill: each workgroup already splits its key range between two wave
+// groups; query tiles are additionally split across workgroups (partials +
+// merge pass) only when the grid holds fewer workgroups than resident slots
+// (one per CU); a split keeps at least kPrefillMinTiles KV tiles.
+constexpr int kPrefillSlotsPerCu = 1;
+constexpr int kPrefillUnitsPerSlot = 1;
+constexpr int kPrefillMinTiles = 8;
 constexpr int kMaxSplitsApi = 256;
 constexpr int kDefaultCuCount = 256;
 constexpr size_t kAlign = 256;
@@ -139,6 +146,56 @@ pa_status run_split(const pa_desc* d, pa::DecodeArgs a, int S, void* workspace, 
   return PA_OK;
 }
 
+// Chunked prefill: query tiles of packed (token, head-in-group) rows, each
+// optionally split along its key range.
+struct PrefillPlan {
+  long long units;      // (request, query tile, KV head) triples in the grid
+  int tiles_per_seq;
+  int splits;           // S
+  int kv_tiles_per_split;
+};
+
+PrefillPlan prefill_plan(const pa_desc* d, int cus) {
+  PrefillPlan pp;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  const int rows = pa::prefill_tile_rows(d->head_dim);
+  pp.tiles_per_seq = (int)(((long long)d->max_q_len * G + rows - 1) / rows);
+  pp.units = (long long)pp.tiles_per_seq * d->num_seqs * d->num_kv_heads;
+  const int keys = pa::prefill_tile_keys();
+  const int max_kv_tiles = (d->max_seq_len + keys - 1) / keys;
+  const long long slots = (long long)kPrefillSlotsPerCu * cus;
+  pp.splits = 1;
+  pp.kv_tiles_per_split = max_kv_tiles > 0 ? max_kv_tiles : 1;
+  if (pp.units > 0 && pp.units < (long long)kPrefillUnitsPerSlot * slots &&
+      max_kv_tiles >= 2 * kPrefillMinTiles) {
+    // aim for about kPrefillUnitsPerSlot splits of roughly half the longest
+    // key range per slot
+    long long want = (pp.units * max_kv_tiles + (long long)kPrefillUnitsPerSlot * slots - 1) /
+                     ((long long)kPrefillUnitsPerSlot * slots);
+    int kc = (int)(want < kPrefillMinTiles ? kPrefillMinTiles : want);
+    int S = (max_kv_tiles + kc - 1) / kc;
+    if (S > kMaxSplits) {
+      S = kMaxSplits;
+      kc = (max_kv_tiles + S - 1) / S;
+    }
+    if (S > 1) {
+      pp.splits = S;
+      pp.kv_tiles_per_split = kc;
+    }
+  }
+  return pp;
+}
+
+size_t prefill_part_o_bytes(const pa_desc* d, const PrefillPlan& pp) {
+  return align_up((size_t)pp.units * pp.splits * pa::prefill_tile_rows(d->head_dim) * d->head_dim *
+                  sizeof(float));
+}
+
+size_t prefill_workspace_bytes(const pa_desc* d, const PrefillPlan& pp) {
+  return prefill_part_o_bytes(d, pp) +
+         align_up((size_t)pp.units * pp.splits * pa::prefill_tile_rows(d->head_dim) * sizeof(float));
+}
+
 }  // namespace
 
 extern "C" {
@@ -168,14 +225,12 @@ pa_status pa_plan(const pa_desc* d, int32_t cu_count, pa_plan_info* plan) {
   const int cus = cu_count > 0 ? cu_count : device_cu_count();
   const int G = d->num_q_heads / d->num_kv_heads;
   if (d->max_q_len > 1) {
-    // chunked prefill: query tiles of packed (token, head-in-group) rows
     if (d->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
-    const int rows = pa::prefill_tile_rows(d->head_dim);
-    const long long tiles = ((long long)d->max_q_len * G + rows - 1) / rows;
+    PrefillPlan pp = prefill_plan(d, cus);
     plan->path = PA_PATH_PREFILL;
-    plan->num_splits = 1;
-    plan->grid_x = (int32_t)(tiles * d->num_seqs * d->num_kv_heads);
-    plan->workspace_bytes = 0;
+    plan->num_splits = pp.splits;
+    plan->grid_x = (int32_t)(pp.units * pp.splits);
+    plan->workspace_bytes = pp.splits > 1 ? prefill_workspace_bytes(d, pp) : 0;
     return PA_OK;
   }
   if (!pa::decode_group_supported(G)) return PA_ERR_UNSUPPORTED;
@@ -239,7 +294,8 @@ pa_status pa_split_merge(const pa_desc* d, const void* q, const void* k_pool, co
 pa_status pa_prefill_chunk(const pa_desc* d, const void* q, const void* k_pool,
                            const void* v_pool, const int32_t* page_table, const int32_t* seq_lens,
                            const int32_t* q_offsets, const int32_t* q_starts, float scale,
-                           void* out, float* lse, void* stream) {
+                           void* out, float* lse, void* workspace, size_t workspace_bytes,
+                           void* stream) {
   pa_status st = check_desc(d);
   if (st != PA_OK) return st;
   if (d->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
@@ -254,8 +310,16 @@ pa_status pa_prefill_chunk(const pa_desc* d, const void* q, const void* k_pool,
   if (out == q) return PA_ERR_ARG;
   if (!(scale > 0.f) || !isfinite(scale)) return PA_ERR_ARG;
   if (d->max_q_len < 1) return PA_ERR_ARG;
-  const int rows = pa::prefill_tile_rows(d->head_dim);
-  const long long tiles = ((long long)d->max_q_len * G + rows - 1) / rows;
+  PrefillPlan pp = prefill_plan(d, device_cu_count());
+  if (workspace == nullptr) {
+    // no scratch: run every query tile over its whole key range
+    pp.splits = 1;
+    pp.kv_tiles_per_split = (d->max_seq_len + pa::prefill_tile_keys() - 1) / pa::prefill_tile_keys();
+    if (pp.kv_tiles_per_split < 1) pp.kv_tiles_per_split = 1;
+  } else if (pp.splits > 1 &&
+             (workspace_bytes < prefill_workspace_bytes(d, pp) || !aligned16(workspace))) {
+    return PA_ERR_WORKSPACE;
+  }
   pa::PrefillArgs a;
   memset(&a, 0, sizeof(a));
   a.q = q;
@@ -272,7 +336,13 @@ pa_status pa_prefill_chunk(const pa_desc* d, const void* q, const void* k_pool,
   a.num_kv_heads = d->num_kv_heads;
   a.max_pages_per_seq = d->max_pages_per_seq;
   a.num_pages = d->num_pages;
-  a.tiles_per_seq = (int32_t)tiles;
+  a.tiles_per_seq = pp.tiles_per_seq;
+  a.num_splits = pp.splits;
+  a.kv_tiles_per_split = pp.kv_tiles_per_split;
+  if (pp.splits > 1) {
+    a.part_o = reinterpret_cast<float*>(workspace);
+    a.part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + prefill_part_o_bytes(d, pp));
+  }
   a.scale_log2 = scale * kLog2e;
   const hipError_t e = pa::launch_prefill(a, d->head_dim, G, reinterpret_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported) return PA_ERR_UNSUPPORTED;

@@ -62,14 +62,20 @@ struct PrefillArgs {
   const int32_t* q_starts;  // [B+1] or null (derived on the device)
   void* out;                // [total_q, Hq, d] bf16
   float* lse;               // [total_q, Hq] or null
+  float* part_o;            // split partials [units, S, tile_rows, d] (S > 1 only)
+  float* part_lse;          // [units, S, tile_rows]
   int32_t num_seqs, num_q_heads, num_kv_heads, max_pages_per_seq;
   int32_t num_pages;
   int32_t tiles_per_seq;    // query tiles per (request, KV head) in the grid
+  int32_t num_splits;       // S: key-range splits per query tile in the grid (1 = unsplit)
+  int32_t kv_tiles_per_split;  // KV tiles one split covers
   float scale_log2;
 };
 
-// Rows of the packed (token, head-in-group) query tile one workgroup owns.
+// Rows of the packed (token, head-in-group) query tile one workgroup owns,
+// and keys per KV tile.
 int prefill_tile_rows(int head_dim);
+int prefill_tile_keys();
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int group, hipStream_t s);
 
 // ---------------------------------------------------------------------------

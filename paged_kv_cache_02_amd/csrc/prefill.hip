@@ -8,26 +8,34 @@
 // matrix is stored.  The G query heads of a KV head are packed token-major:
 // packed row rho = token * G + h, so one K/V tile serves all of them (GQA).
 //
-// Workgroup = 4 waves = one tile of 128 packed rows of one (request, KV
-// head); each wave owns 32 rows.  Keys stream in tiles of 64 (4 pages):
-//   * K tile staged row-major in LDS, V tile staged transposed (V^T, dims x
-//     keys), both double-buffered, loaded into registers one tile ahead;
-//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: A = K rows from LDS, B = Q
-//     held in registers, so every lane ends up owning one query row and 16 of
-//     every 32 keys -- the row max/sum need one exchange with lane ^ 32;
-//   * causal mask by select on the diagonal tiles only; lazy online-softmax
-//     rescale (only when the max grows by more than 2^8);
-//   * P is rounded to bf16 and O^T += V^T P^T with the same MFMA, so the
-//     output accumulator also has one row per lane and the rescale stays
-//     lane-local.
-// The P^T operand comes straight out of the S^T accumulator registers; the
-// key order that implies (within each 16 keys, quads 0 and 2 on the low lane
-// half, 1 and 3 on the high half) is baked into the V^T tile when it is
-// written to LDS, so every MFMA operand read from LDS is one 16-byte load.
+// Work decomposition.  A workgroup of 2 waves owns a tile of 128 packed rows
+// of one (request, KV head) and, when the key range is long, one split of it:
+// the KV tiles of a long row tile are cut into splits of `kv_tiles_per_split`
+// tiles that run as separate workgroups and write partial results which a
+// merge pass combines by log-sum-exp, so long and short row tiles even out
+// across the CUs.
 //
-// Keys at or past seq_len (page tails, possibly NaN) are zeroed while
-// staging, and their scores are masked, so they cannot reach the output;
-// page-table entries past the last needed page are never read.
+// Inside a workgroup, each wave owns 64 rows (two 32-row MFMA blocks that
+// share every operand read from LDS) and keys stream in tiles of 64 (4
+// pages):
+//   * K and V pages are copied straight from HBM into LDS with
+//     global_load_lds (no staging registers), double-buffered one tile
+//     ahead; 16-byte chunks of each key row are XOR-swizzled by key so the
+//     operand reads below are bank-conflict free;
+//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: A = K rows read from LDS,
+//     B = Q held in registers, so a lane owns one query row and 16 of every
+//     32 keys -- the row max and sum need one exchange with lane ^ 32;
+//   * causal mask by select on diagonal tiles only; lazy online-softmax
+//     rescale (only when the max grows by more than 2^8);
+//   * P is rounded to bf16 and O^T += V^T P^T: the V^T operand comes from
+//     V's natural [key][dim] layout through ds_read_b64_tr_b16 (gfx950's
+//     transposing LDS read), in the key order the P^T registers carry, and
+//     the output accumulator keeps one row per lane, so rescaling is local.
+//
+// Keys at or past a row's position are masked by select before the max.  K
+// and V rows of keys at or past seq_len (page tails, possibly NaN) are never
+// loaded: their LDS slots are zero-filled, so no NaN meets a zero weight.
+// Page-table entries past the pages needed are never read.
 #include "pa_internal.h"
 
 #include <math.h>
@@ -35,26 +43,45 @@
 namespace pa {
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kGroups = 2;                        // wave groups splitting a tile's key range
+constexpr int kWavesPerGroup = 4;
+constexpr int kWaves = kGroups * kWavesPerGroup;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRowsPerWave = 32;
-constexpr int kTileRows = kWaves * kRowsPerWave;  // packed (token, head) rows per workgroup
+constexpr int kRB = 1;                            // 32-row MFMA blocks per wave
+constexpr int kRowsPerWave = 32 * kRB;
+constexpr int kTileRows = kWavesPerGroup * kRowsPerWave;  // packed (token, head) rows per workgroup
 constexpr int kTileKeys = 64;                     // keys per KV tile (4 pages)
 constexpr int kPagesPerTile = kTileKeys / kPageSize;
+constexpr int kLdsPages = 2048;                   // page ids kept in LDS
 constexpr float kRescaleLog2 = 8.0f;
 constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kLog2e = 1.4426950408889634f;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short shortx4_t __attribute__((ext_vector_type(4)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 template <int D>
-struct Lds {
-  static constexpr int kKStride = D + 8;           // bf16 per K row (16-byte pad)
-  static constexpr int kVStride = kTileKeys + 8;   // bf16 per V^T row (16-byte pad)
-  static constexpr int kKElems = kTileKeys * kKStride;
-  static constexpr int kVElems = D * kVStride;
-  static constexpr int kBufElems = kKElems + kVElems;
+struct Geo {
+  static constexpr int kRowBytes = D * 2;             // one key row in LDS (no padding)
+  static constexpr int kRowChunks = D / 8;            // 16-byte chunks per key row
+  static constexpr int kKeysPerDma = 64 / kRowChunks; // key rows one 1 KB DMA instruction fills
+  static constexpr int kTileBytes = kTileKeys * kRowBytes;
+  static constexpr int kDmaPerTile = kTileBytes / 1024;  // per K (and per V) tile
+  static constexpr int kKSteps = D / 16;              // MFMA k-steps over the head dim
+  static constexpr int kDimBlocks = D / 32;           // 32-dim output blocks
 };
+
+// XOR swizzle of 16-byte chunk indices within a key row.  For d = 128 (16
+// chunks per 256-byte row, LDS serving 256 bytes per cycle) it is a bijection
+// on 16 consecutive keys, so the 16 rows of one K operand read land on 16
+// different chunks, and its bits 2..3 follow key & 3, so the 4 consecutive
+// keys of one transposing V read land in 4 different 64-byte bank quads.
+template <int D>
+__device__ __forceinline__ int swz(int key) {
+  return D == 128 ? (((key & 3) << 2) | ((key >> 2) & 3)) : ((key >> 1) & 3);
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -68,35 +95,47 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
 
-// Quad permutation applied to V^T columns (see the file comment): within a
-// group of 16 keys, quad q sits at position swap12(q).
-__device__ __forceinline__ int swap12(int q) { return (q == 1) ? 2 : (q == 2 ? 1 : q); }
-
-template <int D>
-struct Staging {
-  static_assert(D == 64 || D == 128, "staging layout is written for head_dim 64 or 128");
-  static constexpr int kKChunks = kTileKeys * D / 8 / kThreads;  // 16-byte K chunks per thread
-  // V: thread (kq = lane % 16, c8 = lane / 16 + 4 * wave) holds keys 4kq..4kq+3
-  // of the tile at dims 8c8..8c8+7; threads with c8 >= D/8 stage nothing
-  uint4 k[kKChunks];
-  uint4 v[4];
+// Geometry of one (request, row tile) shared by the attention kernel and the
+// merge pass.
+struct TileGeo {
+  int L, o, n, rows_total, row_base, kmax, ntiles;
 };
 
-// Page ids.  At kernel start the workgroup copies the page-table entries
-// it needs (clamped into the pool) into LDS, so a tile's 4 page ids are LDS
-// broadcast reads (short, lgkmcnt-tracked) instead of global round trips.
-// A request whose needed pages exceed the LDS copy reads the page table
-// directly (a slower path with the same results).
-constexpr int kLdsPages = 2048;
+__device__ __forceinline__ TileGeo tile_geo(const PrefillArgs& a, int r, int t, int group) {
+  TileGeo tg;
+  tg.L = a.seq_lens[r];
+  tg.o = a.q_offsets[r];
+  tg.n = tg.L - tg.o;
+  tg.rows_total = tg.n * group;
+  tg.row_base = t * kTileRows;
+  const int last_row = min(tg.row_base + kTileRows, tg.rows_total) - 1;
+  tg.kmax = tg.o + last_row / group + 1;   // keys the tile's last row sees
+  tg.ntiles = (tg.kmax + kTileKeys - 1) / kTileKeys;
+  return tg;
+}
 
+__device__ __forceinline__ int num_splits_of(int ntiles, int kv_tiles_per_split) {
+  return (ntiles + kv_tiles_per_split - 1) / kv_tiles_per_split;
+}
+
+// First packed query row of request r (from q_starts, or by summing n over
+// the earlier requests).
+__device__ __forceinline__ int q_start_of(const PrefillArgs& a, int r, int lane) {
+  if (a.q_starts != nullptr) return a.q_starts[r];
+  int acc = 0;
+  for (int i = lane; i < r; i += 64) acc += a.seq_lens[i] - a.q_offsets[i];
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) acc += __shfl_xor(acc, s);
+  return acc;
+}
+
+// Page id of page m of KV tile kt (uniform), or -1 past the needed pages.
 struct PageIds {
-  const int* lds;                  // LDS copy, or null
+  const int* lds;  // LDS copy of the needed page-table slice, clamped; or null
   const int32_t* __restrict__ ptab;
-  int npages;                      // pages the workgroup needs
-  int num_pages;                   // pool size
+  int npages, num_pages;
 };
 
-// Id of page m (uniform) of KV tile kt, or -1 past the needed pages.
 __device__ __forceinline__ int tile_page(const PageIds& pi, int kt, int m) {
   const int lp = kt * kPagesPerTile + m;
   if (lp >= pi.npages) return -1;
@@ -110,331 +149,490 @@ __device__ __forceinline__ int tile_page(const PageIds& pi, int kt, int m) {
   return __builtin_amdgcn_readfirstlane(id);
 }
 
-// Global -> registers for one KV tile kt (first key kb).  K: 16-byte chunk m
-// of thread tid is key m * (256 / (D/8)) + tid / (D/8) of the tile, so the
-// page of each load is uniform per wave; V: wave w stages page w (4 key
-// quads x D/8 dim chunks).  When the whole tile is live the loads are plain;
-// otherwise every load still comes from a valid address (page 0 stands in
-// for a missing page) and dead keys (>= L, or on a missing page) are
-// selected to zero.
+// DMA one KV tile (K and V) from the pool into an LDS stage.  Each of the 4
+// waves of a group moves a quarter of the 1 KB pieces; lane l of a piece fills LDS slot (key, chunk) =
+// (first key + l / kRowChunks, l % kRowChunks) with the key's chunk
+// (l % kRowChunks) ^ swz(key).  Pieces that hold keys at or past L, or lie on
+// a page past the needed ones, are written with ordinary loads of the live
+// keys and zeros for the rest (so a NaN in a page tail never reaches LDS).
 template <int D>
-__device__ __forceinline__ void stage_load(Staging<D>& st, const __bf16* __restrict__ kpool,
-                                           const __bf16* __restrict__ vpool, const PageIds& pi,
-                                           int kt, int L, int Hkv, int g, int tid, int wave) {
+__device__ __forceinline__ void dma_tile(unsigned char* kst, unsigned char* vst,
+                                         const __bf16* __restrict__ kpool,
+                                         const __bf16* __restrict__ vpool, const PageIds& pi,
+                                         int kt, int L, int Hkv, int g, int wave, int lane) {
+  using GE = Geo<D>;
   const size_t blk = (size_t)kPageSize * D;
   const int kb = kt * kTileKeys;
-  const int id0 = tile_page(pi, kt, 0);
-  const int id1 = tile_page(pi, kt, 1);
-  const int id2 = tile_page(pi, kt, 2);
-  const int last_id = tile_page(pi, kt, kPagesPerTile - 1);
-  const bool full = kb + kTileKeys <= L && last_id >= 0;
-  constexpr int kRowChunks = D / 8;                        // 16-byte chunks per key row
-  constexpr int kKeysPerPass = kThreads / kRowChunks;      // keys one pass of 256 threads covers
-  constexpr int kWavesPerPage = kPageSize / (64 / kRowChunks);
+  constexpr int kPerWave = GE::kDmaPerTile / kWavesPerGroup;
 #pragma unroll
-  for (int m = 0; m < Staging<D>::kKChunks; ++m) {
-    const int key = m * kKeysPerPass + tid / kRowChunks;   // key within the tile
-    const int pm = (m * kKeysPerPass) / kPageSize + wave / kWavesPerPage;  // uniform per wave
-    const int id = pm == 0 ? id0 : (pm == 1 ? id1 : (pm == 2 ? id2 : last_id));
-    const int phys = id >= 0 ? id : 0;
-    const __bf16* src = kpool + ((size_t)phys * Hkv + g) * blk + (key % kPageSize) * D +
-                        (tid % kRowChunks) * 8;
-    const uint4 val = *reinterpret_cast<const uint4*>(src);
-    st.k[m] = (full || (id >= 0 && kb + key < L)) ? val : make_uint4(0, 0, 0, 0);
-  }
-  {
-    const int lane = tid & 63;
-    const int kq = lane % 16;
-    const int c8raw = lane / 16 + 4 * wave;
-    const bool active = c8raw < D / 8;
-    const int c8 = active ? c8raw : 0;
-    const int pm = kq / 4;  // page of this key quad within the tile
-    const int id = pm == 0 ? id0 : (pm == 1 ? id1 : (pm == 2 ? id2 : last_id));
-    const int phys = id >= 0 ? id : 0;
-    const __bf16* base = vpool + ((size_t)phys * Hkv + g) * blk + ((4 * kq) % kPageSize) * D + c8 * 8;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint4 val = *reinterpret_cast<const uint4*>(base + j * D);
-      const int key = kb + 4 * kq + j;
-      st.v[j] = (full || (id >= 0 && key < L)) && active ? val : make_uint4(0, 0, 0, 0);
-    }
-  }
-}
-
-// Registers -> LDS buffer: K row-major, V transposed with the quad order of
-// the P^T operand.
-template <int D>
-__device__ __forceinline__ void stage_store(const Staging<D>& st, __bf16* kbuf, __bf16* vbuf,
-                                            int tid) {
-  constexpr int kRowChunks = D / 8;
-  constexpr int kKeysPerPass = kThreads / kRowChunks;
-#pragma unroll
-  for (int m = 0; m < Staging<D>::kKChunks; ++m) {
-    const int key = m * kKeysPerPass + tid / kRowChunks;
-    *reinterpret_cast<uint4*>(kbuf + key * Lds<D>::kKStride + (tid % kRowChunks) * 8) = st.k[m];
-  }
-  {
-    const int wave = tid >> 6;
-    const int lane = tid & 63;
-    const int kq = lane % 16;             // key quad within the tile
-    const int c8 = lane / 16 + 4 * wave;  // 8-dim chunk
-    if (c8 < D / 8) {
-      const int col = 16 * (kq / 4) + 4 * swap12(kq % 4);
-      const uint32_t* k0 = reinterpret_cast<const uint32_t*>(&st.v[0]);
-      const uint32_t* k1 = reinterpret_cast<const uint32_t*>(&st.v[1]);
-      const uint32_t* k2 = reinterpret_cast<const uint32_t*>(&st.v[2]);
-      const uint32_t* k3 = reinterpret_cast<const uint32_t*>(&st.v[3]);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {   // dword w holds dims 2w (low half) and 2w+1 (high half)
-        uint2 lo, hi;
-        lo.x = (k0[w] & 0xFFFFu) | (k1[w] << 16);
-        lo.y = (k2[w] & 0xFFFFu) | (k3[w] << 16);
-        hi.x = (k0[w] >> 16) | (k1[w] & 0xFFFF0000u);
-        hi.y = (k2[w] >> 16) | (k3[w] & 0xFFFF0000u);
-        const int d0 = c8 * 8 + 2 * w;
-        *reinterpret_cast<uint2*>(vbuf + d0 * Lds<D>::kVStride + col) = lo;
-        *reinterpret_cast<uint2*>(vbuf + (d0 + 1) * Lds<D>::kVStride + col) = hi;
+  for (int i = 0; i < kPerWave; ++i) {
+    const int u = wave * kPerWave + i;                   // 1 KB piece of the tile
+    const int key0 = u * GE::kKeysPerDma;                // first key of the piece (tile-relative)
+    const int pm = key0 / kPageSize;                     // page of the piece within the tile
+    const int id = tile_page(pi, kt, pm);
+    const int key = key0 + lane / GE::kRowChunks;        // this lane's key
+    const int chunk = (lane % GE::kRowChunks) ^ swz<D>(key);
+    const bool live = id >= 0 && kb + key < L;
+    const bool all_live = id >= 0 && kb + key0 + GE::kKeysPerDma <= L;
+    unsigned char* kdst = kst + u * 1024;
+    unsigned char* vdst = vst + u * 1024;
+    if (all_live) {
+      const size_t off = ((size_t)id * Hkv + g) * blk + (key % kPageSize) * D + chunk * 8;
+      __builtin_amdgcn_global_load_lds(kpool + off, (lds_void*)kdst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vpool + off, (lds_void*)vdst, 16, 0, 0);
+    } else {
+      // partial piece: ordinary loads of the live keys, zeros elsewhere
+      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+      if (live) {
+        const size_t off = ((size_t)id * Hkv + g) * blk + (key % kPageSize) * D + chunk * 8;
+        kv = *reinterpret_cast<const uint4*>(kpool + off);
+        vv = *reinterpret_cast<const uint4*>(vpool + off);
       }
+      *reinterpret_cast<uint4*>(kdst + lane * 16) = kv;
+      *reinterpret_cast<uint4*>(vdst + lane * 16) = vv;
     }
   }
 }
 
+template <int N>
+struct GroupTag {
+  static constexpr int value = N;
+};
+
 template <int D>
-__global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int group) {
-  constexpr int kKSteps = D / 16;     // MFMA k-steps over the head dim
-  constexpr int kDimBlocks = D / 32;  // 32-dim output blocks
-  __shared__ __align__(16) __bf16 smem[2 * Lds<D>::kBufElems];
+__global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a, int group) {
+  using GE = Geo<D>;
+  static_assert(kRB == 1, "the wave-group merge is written for one row block per wave");
+  // two LDS stages per wave group, each K + V, named statically so the
+  // compiler can tell the tile being copied in from the tile being read
+  __shared__ __align__(1024) unsigned char k_a0[GE::kTileBytes];
+  __shared__ __align__(1024) unsigned char v_a0[GE::kTileBytes];
+  __shared__ __align__(1024) unsigned char k_a1[GE::kTileBytes];
+  __shared__ __align__(1024) unsigned char v_a1[GE::kTileBytes];
+  __shared__ __align__(1024) unsigned char k_b0[GE::kTileBytes];
+  __shared__ __align__(1024) unsigned char v_b0[GE::kTileBytes];
+  __shared__ __align__(1024) unsigned char k_b1[GE::kTileBytes];
+  __shared__ __align__(1024) unsigned char v_b1[GE::kTileBytes];
+  __shared__ int s_pages[kLdsPages];
+  __shared__ float s_ml[kWavesPerGroup][2][64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave_id / kWavesPerGroup;      // which half of the key range
+  const int wave = wave_id % kWavesPerGroup;     // wave within the group: its 32 rows
   const int half = lane >> 5;     // which 8-element k slice this lane feeds
-  const int lrow = lane & 31;     // the query row this lane owns
+  const int lrow = lane & 31;     // the query row (within a 32-row block) this lane owns
 
+  // grid: KV head fastest (a (request, head) pair's tiles share an XCD when
+  // Hkv is a multiple of 8), then split, then row tiles and requests in
+  // reverse so the heavier tiles start first
   const int Hkv = a.num_kv_heads;
   const int T = a.tiles_per_seq;
-  // heavy work first: later tiles of a request see more keys; the KV head is
-  // the fastest-varying index so a (request, head) pair's tiles share an XCD
-  // when Hkv is a multiple of the XCD count
-  const int bid = blockIdx.x;
+  const int S = a.num_splits;
+  int bid = blockIdx.x;
   const int g = bid % Hkv;
-  const int rt = bid / Hkv;
-  const int t = T - 1 - (rt % T);
-  const int r = a.num_seqs - 1 - rt / T;
+  bid /= Hkv;
+  const int split = bid % S;
+  bid /= S;
+  const int t = T - 1 - (bid % T);
+  const int r = a.num_seqs - 1 - bid / T;
 
-  const int L = a.seq_lens[r];
-  const int o = a.q_offsets[r];
-  const int n = L - o;
-  const int rows_total = n * group;
-  const int row_base = t * kTileRows;
-  if (n <= 0 || row_base >= rows_total) return;
+  const TileGeo tg = tile_geo(a, r, t, group);
+  if (tg.n <= 0 || tg.row_base >= tg.rows_total) return;
+  const int nsp = num_splits_of(tg.ntiles, a.kv_tiles_per_split);
+  if (split >= nsp) return;
+  const int kt0 = split * a.kv_tiles_per_split;
+  const int kt1 = min(kt0 + a.kv_tiles_per_split, tg.ntiles);
+  const int q_start = q_start_of(a, r, lane);
 
-  // first packed query row of this request
-  int q_start;
-  if (a.q_starts != nullptr) {
-    q_start = a.q_starts[r];
-  } else {
-    int acc = 0;
-    for (int i = lane; i < r; i += 64) acc += a.seq_lens[i] - a.q_offsets[i];
+  // this lane's two query rows (row blocks rb = 0, 1)
+  const int Hq = a.num_q_heads;
+  const int o = tg.o;
+  int pos[kRB], tok[kRB], hh[kRB];
+  bool row_valid[kRB];
 #pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) acc += __shfl_xor(acc, s);
-    q_start = acc;
+  for (int rb = 0; rb < kRB; ++rb) {
+    const int rho = tg.row_base + wave * kRowsPerWave + rb * 32 + lrow;
+    row_valid[rb] = rho < tg.rows_total;
+    const int rc = row_valid[rb] ? rho : tg.rows_total - 1;
+    tok[rb] = rc / group;
+    hh[rb] = rc % group;
+    pos[rb] = o + tok[rb];
   }
-
-  // keys the workgroup needs: up to the position of its last row
-  const int last_row = min(row_base + kTileRows, rows_total) - 1;
-  const int kmax = o + last_row / group + 1;
-  const int npages = (kmax + kPageSize - 1) / kPageSize;
-  const int ntiles = (kmax + kTileKeys - 1) / kTileKeys;
-
-  // this lane's query row
-  const int rho = row_base + wave * kRowsPerWave + lrow;
-  const bool row_valid = rho < rows_total;
-  const int rho_c = row_valid ? rho : rows_total - 1;
-  const int tok = rho_c / group;
-  const int hh = rho_c % group;
-  const int pos = o + tok;
-  // the wave's rows span positions [pos_lo, pos_hi]
-  const int wrow0 = min(row_base + wave * kRowsPerWave, rows_total - 1);
-  const int wrow1 = min(row_base + wave * kRowsPerWave + kRowsPerWave, rows_total) - 1;
-  const int pos_lo = o + wrow0 / group;
+  const int wrow0 = min(tg.row_base + wave * kRowsPerWave, tg.rows_total - 1);
+  const int wrow1 = min(tg.row_base + wave * kRowsPerWave + kRowsPerWave, tg.rows_total) - 1;
+  const int pos_lo = o + wrow0 / group;   // the wave's rows span positions [pos_lo, pos_hi]
   const int pos_hi = o + wrow1 / group;
 
-  const int Hq = a.num_q_heads;
   const __bf16* __restrict__ qp = reinterpret_cast<const __bf16*>(a.q);
-  const __bf16* qrow = qp + ((size_t)(q_start + tok) * Hq + (size_t)g * group + hh) * D;
-  uint4 qv[kKSteps];
+  uint4 qv[kRB][GE::kKSteps];
 #pragma unroll
-  for (int s = 0; s < kKSteps; ++s)
-    qv[s] = *reinterpret_cast<const uint4*>(qrow + 16 * s + 8 * half);
+  for (int rb = 0; rb < kRB; ++rb) {
+    const __bf16* qrow = qp + ((size_t)(q_start + tok[rb]) * Hq + (size_t)g * group + hh[rb]) * D;
+#pragma unroll
+    for (int s = 0; s < GE::kKSteps; ++s)
+      qv[rb][s] = *reinterpret_cast<const uint4*>(qrow + 16 * s + 8 * half);
+  }
 
   const __bf16* __restrict__ kpool = reinterpret_cast<const __bf16*>(a.k_pool);
   const __bf16* __restrict__ vpool = reinterpret_cast<const __bf16*>(a.v_pool);
   const int32_t* __restrict__ ptab = a.page_table + (size_t)r * a.max_pages_per_seq;
-  const int npages_c = min(npages, a.max_pages_per_seq);
+  const int npages = min((tg.kmax + kPageSize - 1) / kPageSize, a.max_pages_per_seq);
 
-  floatx16_t oacc[kDimBlocks];
+  PageIds pi;
+  pi.ptab = ptab;
+  pi.npages = npages;
+  pi.num_pages = a.num_pages;
+  pi.lds = nullptr;
+  const int p0 = kt0 * kPagesPerTile;
+  const int p1 = min(kt1 * kPagesPerTile, npages);
+  if (p1 - p0 <= kLdsPages) {
+    for (int i = p0 + tid; i < p1; i += kThreads) {
+      int id = ptab[i];
+      s_pages[i - p0] = id < 0 ? 0 : (id >= a.num_pages ? a.num_pages - 1 : id);
+    }
+    pi.lds = s_pages - p0;   // indexed by logical page
+    __syncthreads();
+  }
+
+  floatx16_t oacc[kRB][GE::kDimBlocks];
 #pragma unroll
-  for (int db = 0; db < kDimBlocks; ++db)
+  for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-  float m_run = -INFINITY;
-  float l_run = 0.f;
+    for (int db = 0; db < GE::kDimBlocks; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[rb][db][i] = 0.f;
+  float m_run[kRB], l_run[kRB];
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) {
+    m_run[rb] = -INFINITY;
+    l_run[rb] = 0.f;
+  }
   const float sl2 = a.scale_log2;
 
-  // one KV tile: S^T, mask, online softmax, O^T += V^T P^T (reads LDS only)
-  auto compute_tile = [&](const __bf16* kbuf, int kb) {
-    const __bf16* vbuf = kbuf + Lds<D>::kKElems;
-    if (kb <= pos_hi) {  // some key of the tile is visible to some row of this wave
-      // ---- S^T = K Q^T over two 32-key blocks ----
-      floatx16_t sacc[2];
+  // lanes of a 16-lane group address 4 keys x 4 dim quads for the
+  // transposing reads of the V^T operand
+  const int vgrp = lane >> 4;
+  const int vp = lane & 15;
+  const int vk = vp >> 2;                                 // which of the 4 keys
+  const int vdim_off = 16 * (vgrp & 1) + 4 * (vp & 3);   // dims within a 32-dim block
+
+  // one KV tile out of an LDS stage
+  auto compute_tile = [&](const unsigned char* kst, const unsigned char* vst, int kb)
+                          __attribute__((always_inline)) {
+    if (kb > pos_hi) return;   // no key of the tile is visible to any row of this wave
+    // ---- S^T = K Q^T: 2 key blocks x 2 row blocks ----
+    // K operand address for k-step s: the swizzled chunk 2s + half of key
+    // row kb2*32 + lrow sits at kbase ^ (32 s) (the swizzle is an XOR on
+    // chunk bits 1..3, and the row base is a multiple of 256 bytes).
+    floatx16_t sacc[kRB][2];
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-        const __bf16* krow = kbuf + (kb2 * 32 + lrow) * Lds<D>::kKStride + 8 * half;
-        const floatx16_t zero = {};
-        sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            as_bf16x8(*reinterpret_cast<const uint4*>(krow)), as_bf16x8(qv[0]), zero, 0, 0, 0);
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      const int key = kb2 * 32 + lrow;
+      const int sw = swz<D>(key);
+      uint32_t kbase = (uint32_t)(key * GE::kRowBytes) + ((uint32_t)(half ^ (sw & 1)) << 4) +
+                       ((uint32_t)(sw >> 1) << 5);
+      asm volatile("" : "+v"(kbase));   // keep the per-step addresses out of the loop preheader
 #pragma unroll
-        for (int s = 1; s < kKSteps; ++s) {
-          const uint4 kv = *reinterpret_cast<const uint4*>(krow + 16 * s);
-          sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), as_bf16x8(qv[s]),
-                                                              sacc[kb2], 0, 0, 0);
+      for (int s = 0; s < GE::kKSteps; ++s) {
+        const uint4 kv = *reinterpret_cast<const uint4*>(kst + (kbase ^ (uint32_t)(s << 5)));
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) {
+          if (s == 0) {
+            const floatx16_t zero = {};
+            sacc[rb][kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), as_bf16x8(qv[rb][0]),
+                                                                    zero, 0, 0, 0);
+          } else {
+            sacc[rb][kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), as_bf16x8(qv[rb][s]),
+                                                                    sacc[rb][kb2], 0, 0, 0);
+          }
         }
       }
-      // ---- causal mask (diagonal tiles only), tile max on raw scores ----
+    }
+    // ---- mask, online softmax, P^T operand ----
+    uint32_t pk[kRB][2][8];
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) {
       if (kb + kTileKeys - 1 > pos_lo) {
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = kb + kb2 * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-            sacc[kb2][i] = key <= pos ? sacc[kb2][i] : -INFINITY;
+            sacc[rb][kb2][i] = key <= pos[rb] ? sacc[rb][kb2][i] : -INFINITY;
           }
       }
       float tmax = -INFINITY;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[kb2][i]);
+        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[rb][kb2][i]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * sl2;   // scale > 0 commutes with max
-      // ---- lazy online-softmax rescale (m_run is in scaled log2 units) ----
-      const bool need = tmax > m_run + kRescaleLog2;
+      const bool need = tmax > m_run[rb] + kRescaleLog2;
       if (__builtin_expect(__any(need), 0)) {
-        const float mn = fmaxf(m_run, tmax);
-        const float alpha = (mn == m_run) ? 1.f : fast_exp2(m_run - mn);
-        l_run *= alpha;
+        const float mn = fmaxf(m_run[rb], tmax);
+        const float alpha = (mn == m_run[rb]) ? 1.f : fast_exp2(m_run[rb] - mn);
+        l_run[rb] *= alpha;
 #pragma unroll
-        for (int db = 0; db < kDimBlocks; ++db)
+        for (int db = 0; db < GE::kDimBlocks; ++db)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-        m_run = mn;
+          for (int i = 0; i < 16; ++i) oacc[rb][db][i] *= alpha;
+        m_run[rb] = mn;
       }
-      // ---- probabilities p = exp2(s * scale_log2 - m), packed to bf16 as P^T ----
-      // m_run is finite here: key 0 is visible to every row, so the first
-      // tile sets it; masked scores are -inf and exp2(-inf) = 0.
-      uint32_t pk[2][8];
+      // a row with no visible key so far keeps m = -inf: use 0 as the
+      // reference so its (all -inf) scores give p = 0 rather than NaN
+      const float mref = m_run[rb] == -INFINITY ? 0.f : m_run[rb];
       float lsum = 0.f;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
-          const float p0 = fast_exp2(fmaf(sacc[kb2][i], sl2, -m_run));
-          const float p1 = fast_exp2(fmaf(sacc[kb2][i + 1], sl2, -m_run));
+          const float p0 = fast_exp2(fmaf(sacc[rb][kb2][i], sl2, -mref));
+          const float p1 = fast_exp2(fmaf(sacc[rb][kb2][i + 1], sl2, -mref));
           lsum += p0 + p1;
-          pk[kb2][i / 2] = pack_bf16x2(p0, p1);
+          pk[rb][kb2][i / 2] = pack_bf16x2(p0, p1);
         }
       }
-      l_run += lsum;
-      // ---- O^T += V^T P^T: 4 k-steps of 16 keys ----
+      l_run[rb] += lsum;
+    }
+    // ---- O^T += V^T P^T: 4 k-steps of 16 keys, 2 row blocks ----
+    // V operand: two transposing 8-byte reads per (k-step, dim block); with
+    // the XOR swizzle the address of dim block db is vbase ^ (64 db).
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int kb2 = ks / 2;
-        const int th = ks % 2;
-        uint4 pb;
-        pb.x = pk[kb2][4 * th + 0];
-        pb.y = pk[kb2][4 * th + 1];
-        pb.z = pk[kb2][4 * th + 2];
-        pb.w = pk[kb2][4 * th + 3];
-        const __bf16* vcol = vbuf + 32 * kb2 + 16 * th + 8 * half;
+    for (int ks = 0; ks < 4; ++ks) {
+      const int kb2 = ks >> 1;
+      const int th = ks & 1;
+      // keys this lane addresses for the two transposing reads (e = 0..3, 4..7)
+      const int keyA = kb2 * 32 + 16 * th + 4 * half + vk;
+      const int keyB = keyA + 8;
+      const int c0 = vdim_off >> 3;                 // chunk of dims within a 32-dim block
+      const int within = (vdim_off & 7) * 2;        // byte offset inside the chunk
+      const int swA = swz<D>(keyA);
+      const int swB = swz<D>(keyB);
+      uint32_t vbaseA = (uint32_t)(keyA * GE::kRowBytes) +
+                        (((uint32_t)(c0 ^ (swA & 3)) << 4) | ((uint32_t)(swA & ~3) << 4)) + within;
+      uint32_t vbaseB = (uint32_t)(keyB * GE::kRowBytes) +
+                        (((uint32_t)(c0 ^ (swB & 3)) << 4) | ((uint32_t)(swB & ~3) << 4)) + within;
+      asm volatile("" : "+v"(vbaseA), "+v"(vbaseB));
+      uint4 pb[kRB];
 #pragma unroll
-        for (int db = 0; db < kDimBlocks; ++db) {
-          const uint4 va = *reinterpret_cast<const uint4*>(vcol + (db * 32 + lrow) * Lds<D>::kVStride);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), as_bf16x8(pb), oacc[db],
-                                                             0, 0, 0);
-        }
+      for (int rb = 0; rb < kRB; ++rb) {
+        pb[rb].x = pk[rb][kb2][4 * th + 0];
+        pb[rb].y = pk[rb][kb2][4 * th + 1];
+        pb[rb].z = pk[rb][kb2][4 * th + 2];
+        pb[rb].w = pk[rb][kb2][4 * th + 3];
+      }
+#pragma unroll
+      for (int db = 0; db < GE::kDimBlocks; ++db) {
+        const shortx4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) shortx4_t*)(vst + (vbaseA ^ (uint32_t)(db << 6))));
+        const shortx4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) shortx4_t*)(vst + (vbaseB ^ (uint32_t)(db << 6))));
+        uint4 av;
+        av.x = __builtin_bit_cast(uint32_t, __builtin_shufflevector(va, va, 0, 1));
+        av.y = __builtin_bit_cast(uint32_t, __builtin_shufflevector(va, va, 2, 3));
+        av.z = __builtin_bit_cast(uint32_t, __builtin_shufflevector(vb, vb, 0, 1));
+        av.w = __builtin_bit_cast(uint32_t, __builtin_shufflevector(vb, vb, 2, 3));
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb)
+          oacc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(pb[rb]),
+                                                                 oacc[rb][db], 0, 0, 0);
       }
     }
   };
 
-  // Software pipeline over KV tiles, two tiles of loads in flight: while
-  // tile kt is computed out of one LDS buffer, tile kt+1 sits in one set of
-  // staging registers (loaded during the previous step) and tile kt+2 is
-  // being loaded into the other.  Prefetch loads past the last tile read a
-  // valid stand-in page and are never stored.  Unrolled by two so that the
-  // staging register sets and LDS buffers are indexed statically.
-  __shared__ int s_pages[kLdsPages];
-  PageIds pi;
-  pi.ptab = ptab;
-  pi.npages = npages_c;
-  pi.num_pages = a.num_pages;
-  pi.lds = nullptr;
-  if (npages_c <= kLdsPages) {
-    for (int i = tid; i < npages_c; i += kThreads) {
-      int id = ptab[i];
-      s_pages[i] = id < 0 ? 0 : (id >= a.num_pages ? a.num_pages - 1 : id);
+  // The two wave groups take the two halves of the key range, [kt0, mid)
+  // and [mid, kt1), over the same rows.  Per group: tile i is computed out of
+  // one LDS stage while tile i+1 is copied into the other by DMA; a barrier
+  // per step (shared by both groups, which run the same number of steps)
+  // hands stages over.  Unrolled by two so each step names its stages.
+  const int L = tg.L;
+  const int mid = kt0 + (kt1 - kt0 + 1) / 2;
+  const int nloop = mid - kt0;
+  auto run = [&](auto gtag) __attribute__((always_inline)) {
+    constexpr int GRP = decltype(gtag)::value;
+    unsigned char* ks0 = GRP == 0 ? k_a0 : k_b0;
+    unsigned char* vs0 = GRP == 0 ? v_a0 : v_b0;
+    unsigned char* ks1 = GRP == 0 ? k_a1 : k_b1;
+    unsigned char* vs1 = GRP == 0 ? v_a1 : v_b1;
+    const int my0 = GRP == 0 ? kt0 : mid;
+    const int my1 = GRP == 0 ? mid : kt1;
+    if (my0 < my1) dma_tile<D>(ks0, vs0, kpool, vpool, pi, my0, L, Hkv, g, wave, lane);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int i = 0;;) {
+      int kt = my0 + i;
+      if (kt + 1 < my1) dma_tile<D>(ks1, vs1, kpool, vpool, pi, kt + 1, L, Hkv, g, wave, lane);
+      if (kt < my1) compute_tile(ks0, vs0, kt * kTileKeys);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (++i >= nloop) break;
+      kt = my0 + i;
+      if (kt + 1 < my1) dma_tile<D>(ks0, vs0, kpool, vpool, pi, kt + 1, L, Hkv, g, wave, lane);
+      if (kt < my1) compute_tile(ks1, vs1, kt * kTileKeys);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (++i >= nloop) break;
     }
-    pi.lds = s_pages;
-    __syncthreads();
-  }
-  Staging<D> sA, sB;
-  stage_load<D>(sA, kpool, vpool, pi, 0, L, Hkv, g, tid, wave);
-  stage_load<D>(sB, kpool, vpool, pi, 1, L, Hkv, g, tid, wave);
-  __bf16* buf0 = smem;
-  __bf16* buf1 = smem + Lds<D>::kBufElems;
-  stage_store<D>(sA, buf0, buf0 + Lds<D>::kKElems, tid);
-  __syncthreads();
+  };
+  if (grp == 0)
+    run(GroupTag<0>{});
+  else
+    run(GroupTag<1>{});
 
-  for (int kt = 0;;) {
-    // even step: tile kt in buf0, tile kt+1 in sB, tile kt+2 -> sA
-    stage_load<D>(sA, kpool, vpool, pi, kt + 2, L, Hkv, g, tid, wave);
-    compute_tile(buf0, kt * kTileKeys);
-    if (kt + 1 < ntiles) stage_store<D>(sB, buf1, buf1 + Lds<D>::kKElems, tid);
-    __syncthreads();
-    if (++kt >= ntiles) break;
-    // odd step: tile kt in buf1, tile kt+1 in sA, tile kt+2 -> sB
-    stage_load<D>(sB, kpool, vpool, pi, kt + 2, L, Hkv, g, tid, wave);
-    compute_tile(buf1, kt * kTileKeys);
-    if (kt + 1 < ntiles) stage_store<D>(sA, buf0, buf0 + Lds<D>::kKElems, tid);
-    __syncthreads();
-    if (++kt >= ntiles) break;
-  }
-
-  // ---- normalize and write ----
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (row_valid) {
-    const float inv = 1.f / l_tot;
-    __bf16* orow = reinterpret_cast<__bf16*>(a.out) + ((size_t)(q_start + tok) * Hq + (size_t)g * group + hh) * D;
+  // ---- merge the groups: group 1 hands its per-lane state to group 0 ----
+  // Every lane of both groups owns the same (row, dims), so the merge is the
+  // log-sum-exp rule applied lane by lane.  Group 1's stage buffers are free
+  // now (the last barrier above ended all reads); wave w of the group writes
+  // its accumulator into one of them, float4 j of lane l at j*1024 + l*16.
+  {
+    unsigned char* xfer = wave == 0 ? k_b0 : (wave == 1 ? v_b0 : (wave == 2 ? k_b1 : v_b1));
+    if (grp == 1) {
 #pragma unroll
-    for (int db = 0; db < kDimBlocks; ++db) {
+      for (int db = 0; db < GE::kDimBlocks; ++db)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float4 w;
+          w.x = oacc[0][db][4 * v + 0];
+          w.y = oacc[0][db][4 * v + 1];
+          w.z = oacc[0][db][4 * v + 2];
+          w.w = oacc[0][db][4 * v + 3];
+          *reinterpret_cast<float4*>(xfer + (db * 4 + v) * 1024 + lane * 16) = w;
+        }
+      s_ml[wave][0][lane] = m_run[0];
+      s_ml[wave][1][lane] = l_run[0];
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    const float mB = s_ml[wave][0][lane];
+    const float lB = s_ml[wave][1][lane];
+    const float M = fmaxf(m_run[0], mB);
+    const float fA = m_run[0] == -INFINITY ? 0.f : fast_exp2(m_run[0] - M);
+    const float fB = mB == -INFINITY ? 0.f : fast_exp2(mB - M);
+#pragma unroll
+    for (int db = 0; db < GE::kDimBlocks; ++db)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        uint2 w;
-        w.x = pack_bf16x2(oacc[db][4 * v + 0] * inv, oacc[db][4 * v + 1] * inv);
-        w.y = pack_bf16x2(oacc[db][4 * v + 2] * inv, oacc[db][4 * v + 3] * inv);
-        *reinterpret_cast<uint2*>(orow + db * 32 + 8 * v + 4 * half) = w;
+        const float4 w = *reinterpret_cast<const float4*>(xfer + (db * 4 + v) * 1024 + lane * 16);
+        oacc[0][db][4 * v + 0] = oacc[0][db][4 * v + 0] * fA + w.x * fB;
+        oacc[0][db][4 * v + 1] = oacc[0][db][4 * v + 1] * fA + w.y * fB;
+        oacc[0][db][4 * v + 2] = oacc[0][db][4 * v + 2] * fA + w.z * fB;
+        oacc[0][db][4 * v + 3] = oacc[0][db][4 * v + 3] * fA + w.w * fB;
       }
+    l_run[0] = l_run[0] * fA + lB * fB;
+    m_run[0] = M;
+  }
+
+  // ---- normalize and write: final output, or this split's partial ----
+  const bool partial = nsp > 1;
+  const size_t unit = ((size_t)r * T + t) * Hkv + g;
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) {
+    const float l_tot = l_run[rb] + __shfl_xor(l_run[rb], 32);
+    if (!row_valid[rb]) continue;
+    const bool empty = !(l_tot > 0.f);
+    const float inv = empty ? 0.f : 1.f / l_tot;
+    const float lse = empty ? -INFINITY : (m_run[rb] + __log2f(l_tot)) * kLn2;
+    if (!partial) {
+      __bf16* orow = reinterpret_cast<__bf16*>(a.out) +
+                     ((size_t)(q_start + tok[rb]) * Hq + (size_t)g * group + hh[rb]) * D;
+#pragma unroll
+      for (int db = 0; db < GE::kDimBlocks; ++db)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          uint2 w;
+          w.x = pack_bf16x2(oacc[rb][db][4 * v + 0] * inv, oacc[rb][db][4 * v + 1] * inv);
+          w.y = pack_bf16x2(oacc[rb][db][4 * v + 2] * inv, oacc[rb][db][4 * v + 3] * inv);
+          *reinterpret_cast<uint2*>(orow + db * 32 + 8 * v + 4 * half) = w;
+        }
+      if (a.lse != nullptr && half == 0)
+        a.lse[(size_t)(q_start + tok[rb]) * Hq + (size_t)g * group + hh[rb]] = lse;
+    } else {
+      const int prow = wave * kRowsPerWave + rb * 32 + lrow;   // row within the tile
+      const size_t pidx = (unit * S + split) * kTileRows + prow;
+      float* po = a.part_o + pidx * D;
+#pragma unroll
+      for (int db = 0; db < GE::kDimBlocks; ++db)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float4 w;
+          w.x = oacc[rb][db][4 * v + 0] * inv;
+          w.y = oacc[rb][db][4 * v + 1] * inv;
+          w.z = oacc[rb][db][4 * v + 2] * inv;
+          w.w = oacc[rb][db][4 * v + 3] * inv;
+          *reinterpret_cast<float4*>(po + db * 32 + 8 * v + 4 * half) = w;
+        }
+      if (half == 0) a.part_lse[pidx] = lse;
     }
-    if (a.lse != nullptr && half == 0)
-      a.lse[(size_t)(q_start + tok) * Hq + (size_t)g * group + hh] = (m_run + __log2f(l_tot)) * kLn2;
+  }
+}
+
+// Merge pass for split row tiles: one workgroup per (request, row tile, KV
+// head); each wave takes rows, each lane D/64 dims.  LSE = M + ln sum_s
+// exp(lse_s - M), out = sum_s exp(lse_s - LSE) * O_s.
+template <int D>
+__global__ void __launch_bounds__(256) prefill_merge_kernel(PrefillArgs a, int group) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int Hkv = a.num_kv_heads;
+  const int T = a.tiles_per_seq;
+  const int S = a.num_splits;
+  int bid = blockIdx.x;
+  const int g = bid % Hkv;
+  bid /= Hkv;
+  const int t = bid % T;
+  const int r = bid / T;
+  const TileGeo tg = tile_geo(a, r, t, group);
+  if (tg.n <= 0 || tg.row_base >= tg.rows_total) return;
+  const int nsp = num_splits_of(tg.ntiles, a.kv_tiles_per_split);
+  if (nsp <= 1) return;
+  const int q_start = q_start_of(a, r, lane);
+  const int Hq = a.num_q_heads;
+  const size_t unit = ((size_t)r * T + t) * Hkv + g;
+  constexpr int kPer = D / 64;
+  for (int prow = wave; prow < kTileRows; prow += 4) {
+    const int rho = tg.row_base + prow;
+    if (rho >= tg.rows_total) break;
+    float M = -INFINITY;
+    for (int s = 0; s < nsp; ++s) M = fmaxf(M, a.part_lse[(unit * S + s) * kTileRows + prow]);
+    const float Mb = M == -INFINITY ? 0.f : M;
+    float tot = 0.f;
+    for (int s = 0; s < nsp; ++s) {
+      const float v = a.part_lse[(unit * S + s) * kTileRows + prow];
+      tot += v == -INFINITY ? 0.f : exp2f((v - Mb) * kLog2e);
+    }
+    const float LSE = Mb + logf(tot);
+    float acc[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) acc[i] = 0.f;
+    for (int s = 0; s < nsp; ++s) {
+      const size_t pidx = (unit * S + s) * kTileRows + prow;
+      const float v = a.part_lse[pidx];
+      const float w = v == -INFINITY ? 0.f : exp2f((v - LSE) * kLog2e);
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) acc[i] = fmaf(w, a.part_o[pidx * D + lane + 64 * i], acc[i]);
+    }
+    const int tok = rho / group;
+    const int hh = rho % group;
+    const size_t orow = (size_t)(q_start + tok) * Hq + (size_t)g * group + hh;
+    __bf16* out = reinterpret_cast<__bf16*>(a.out) + orow * D;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) out[lane + 64 * i] = (__bf16)acc[i];
+    if (a.lse != nullptr && lane == 0) a.lse[orow] = LSE;
   }
 }
 
 template <int D>
 hipError_t launch_d(const PrefillArgs& a, int group, hipStream_t s) {
-  const long long grid = (long long)a.num_seqs * a.tiles_per_seq * a.num_kv_heads;
+  const long long units = (long long)a.num_seqs * a.tiles_per_seq * a.num_kv_heads;
+  const long long grid = units * a.num_splits;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(prefill_kernel<D>, dim3((unsigned)grid), dim3(kThreads), 0, s, a, group);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.num_splits <= 1) return e;
+  hipLaunchKernelGGL(prefill_merge_kernel<D>, dim3((unsigned)units), dim3(256), 0, s, a, group);
   return hipGetLastError();
 }
 
@@ -444,6 +642,8 @@ int prefill_tile_rows(int head_dim) {
   (void)head_dim;
   return kTileRows;
 }
+
+int prefill_tile_keys() { return kTileKeys; }
 
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int group, hipStream_t s) {
   if (group < 1 || group > 16) return hipErrorNotSupported;

@@ -99,7 +99,7 @@ def test_entry_points_reject_null_pointers_without_touching_the_device():
     assert rc == pa.PA_ERR_ARG
     dp = desc(max_q_len=64, total_q=64)
     rc = L.pa_prefill_chunk(ctypes.byref(dp), None, None, None, None, None, None, None, 0.1, None,
-                            None, None)
+                            None, None, 0, None)
     assert rc == pa.PA_ERR_ARG
     rc = L.pa_merge_partials(4, 8, 2, 128, None, None, None, pa.PA_BF16, None, None)
     assert rc == pa.PA_ERR_ARG
