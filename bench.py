@@ -44,7 +44,38 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0,
                     help="wall-clock budget of the oracle's CPU baseline sample")
+    ap.add_argument("--mode", choices=("step", "copy"), default="step",
+                    help="step: the benchmark; copy: calibration of the HBM counters and "
+                         "the streaming ceiling (a plain 1 GiB device copy and a read-only "
+                         "reduction of known size)")
     return ap.parse_args()
+
+
+def copy_calibration(steps: int):
+    """A plain copy of 1 GiB (1 GiB read + 1 GiB written per launch) and a
+    read-only sum over 2 GiB, timed with events.  rocprofv3 counter runs of
+    this mode give the bytes FETCH_SIZE / WRITE_SIZE report for known
+    traffic, which scales the counters of the attention kernels."""
+    import torch
+    n = 1 << 28
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    big = torch.ones(1 << 29, dtype=torch.float32, device="cuda")
+    res = {}
+    for name, fn, nbytes in (("copy_1GiB", lambda: y.copy_(x), 2 * n * 4),
+                             ("sum_2GiB", lambda: big.sum(), (1 << 29) * 4)):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        res[name] = {"us": round(us, 2), "GB/s": round(nbytes / us / 1e3, 1), "bytes": nbytes}
+    print(json.dumps({"calibration": res}), flush=True)
 
 
 def source_hash(*names) -> str:
@@ -147,6 +178,9 @@ def main():
     import paged_kv_cache_02_amd as pa
     import workloads as W
 
+    if args.mode == "copy":
+        copy_calibration(args.steps)
+        return
     torch.cuda.init()
     dev = torch.device("cuda:0")
     full = W.make_config(WORKLOAD, seed=args.seed, poison=False)
@@ -174,13 +208,16 @@ def main():
     dc_out = torch.empty_like(dc_t["q"])
     dc_lse = torch.empty(dc.total_q, dc.num_q_heads, dtype=torch.float32, device=dev)
     ws = torch.empty(max(dc_plan["workspace_bytes"], 256), dtype=torch.uint8, device=dev)
+    pf_ws = (torch.empty(pf_plan["workspace_bytes"], dtype=torch.uint8, device=dev)
+             if pf_plan["workspace_bytes"] else None)
 
     def step(i, ev=None):
         kp, vp = pools[i & 1]
         if ev is not None:
             ev[0].record()
         pa.pa_prefill_chunk(pf_t["q"], kp, vp, pf_t["pt"], pf_t["sl"], pf_t["qo"], pf.scale,
-                            q_starts=pf_t["qs"], out=pf_out, lse=pf_lse, desc=pf_desc)
+                            q_starts=pf_t["qs"], out=pf_out, lse=pf_lse, workspace=pf_ws,
+                            desc=pf_desc)
         if ev is not None:
             ev[1].record()
         pa.pa_decode(dc_t["q"], kp, vp, dc_t["pt"], dc_t["sl"], dc_t["qo"], dc.scale,

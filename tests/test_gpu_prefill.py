@@ -121,3 +121,24 @@ def test_repeated_runs_are_bit_identical():
     o1, l1 = run_prefill(b, dev)
     o2, l2 = run_prefill(b, dev)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_long_context_short_chunk_splits_across_workgroups():
+    # one short chunk deep into a long context: few query tiles, so the guard
+    # also splits each tile's key range across workgroups (partials + merge
+    # pass); the unsplit route must agree with the oracle too
+    b = chunk_batch(58, [4100, 2500], [4036, 2480], 32, 8, 128)
+    dev = device_batch(b)
+    desc = pa.make_desc(dev["q"], dev["k_pool"], dev["page_table"], dev["seq_lens"], b.max_seq_len,
+                        b.max_q_len)
+    plan = pa.pa_plan(desc)
+    print(f"case short chunk deep in context plan={plan}", flush=True)
+    assert plan["num_splits"] > 1 and plan["workspace_bytes"] > 0
+    ro, rl = oracle_run(b)
+    out, lse = run_prefill(b, dev)
+    compare(b, out, lse, ro, rl, label="prefill split across workgroups")
+    out2, lse2 = pa.pa_prefill_chunk(dev["q"], dev["k_pool"], dev["v_pool"], dev["page_table"],
+                                     dev["seq_lens"], dev["q_offsets"], b.scale, split=False,
+                                     max_seq_len=b.max_seq_len, max_q_len=b.max_q_len)
+    torch.cuda.synchronize()
+    compare(b, out2, lse2, ro, rl, label="prefill unsplit")
