@@ -9,6 +9,10 @@ Qwen3-4B attention heads: 4 prefill chunks of 512 tokens at prior offsets
 8 KV heads, d = 128, bf16, page size 16, permuted pool of 1.25x the pages.
 Inputs are synthetic N(0,1) (there are no weights or datasets here).
 
+The timed steps launch the two routes through calls whose arguments are
+marshalled once, so the host stays ahead of the GPU and the kernels run back
+to back; events between the routes time each route on the launch stream.
+
 Prints ONE JSON line.  `value` is the decode path's algorithmic KV GB/s; the
 prefill path's algorithmic TFLOP/s is reported beside it, and `roofline`
 describes whichever kernel takes the larger share of the step.  Two copies
@@ -211,17 +215,25 @@ def main():
     pf_ws = (torch.empty(pf_plan["workspace_bytes"], dtype=torch.uint8, device=dev)
              if pf_plan["workspace_bytes"] else None)
 
+    # the two routes on each pool copy, with their arguments marshalled once
+    # so that the host stays ahead of the GPU and the kernels run back to back
+    calls = {}
+    for i in (0, 1):
+        kp, vp = pools[i]
+        calls[("prefill", i)] = pa.bind_prefill_chunk(
+            pf_t["q"], kp, vp, pf_t["pt"], pf_t["sl"], pf_t["qo"], pf.scale, q_starts=pf_t["qs"],
+            out=pf_out, lse=pf_lse, workspace=pf_ws, desc=pf_desc)
+        calls[("decode", i)] = pa.bind_decode(
+            dc_t["q"], kp, vp, dc_t["pt"], dc_t["sl"], dc_t["qo"], dc.scale, out=dc_out,
+            lse=dc_lse, workspace=ws, desc=dc_desc)
+
     def step(i, ev=None):
-        kp, vp = pools[i & 1]
         if ev is not None:
             ev[0].record()
-        pa.pa_prefill_chunk(pf_t["q"], kp, vp, pf_t["pt"], pf_t["sl"], pf_t["qo"], pf.scale,
-                            q_starts=pf_t["qs"], out=pf_out, lse=pf_lse, workspace=pf_ws,
-                            desc=pf_desc)
+        calls[("prefill", i & 1)]()
         if ev is not None:
             ev[1].record()
-        pa.pa_decode(dc_t["q"], kp, vp, dc_t["pt"], dc_t["sl"], dc_t["qo"], dc.scale,
-                     out=dc_out, lse=dc_lse, workspace=ws, desc=dc_desc)
+        calls[("decode", i & 1)]()
         if ev is not None:
             ev[2].record()
 
@@ -229,7 +241,8 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # timed region: exactly `steps` steps, events between the launches
+    # timed region: exactly `steps` steps, events between the routes on the
+    # stream the routes are launched on
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -256,7 +269,9 @@ def main():
         "decode": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
                    "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                    "traffic": load_traffic("decode", dc_hash), "ms": round(dc_ms, 4),
-                   "kernel": f"decode_kernel<bf16,128,4> x{dc_plan['num_splits']} splits + merge_kernel",
+                   "kernel": ("decode_balanced_kernel<bf16,128,4> + merge_kernel"
+                              if dc_plan["path"] == "decode_balanced" else
+                              f"decode_kernel<bf16,128,4> x{dc_plan['num_splits']} + merge_kernel"),
                    "work": dec_bytes, "work_unit": "B"},
     }
     dominant = "prefill" if pf_ms >= dc_ms else "decode"

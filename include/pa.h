@@ -73,9 +73,10 @@ typedef enum pa_dtype { PA_BF16 = 0, PA_F32 = 1 } pa_dtype;
 
 /* Routes chosen by the dispatch guard. */
 typedef enum pa_path {
-  PA_PATH_DECODE = 0,        /* one workgroup per (request, KV head)           */
-  PA_PATH_DECODE_SPLIT = 1,  /* split-K partitions + log-sum-exp merge pass    */
-  PA_PATH_PREFILL = 2        /* query tiles through LDS-staged bf16 MFMA       */
+  PA_PATH_DECODE = 0,          /* one workgroup per (request, KV head)                   */
+  PA_PATH_DECODE_SPLIT = 1,    /* equal split-K partitions + log-sum-exp merge pass      */
+  PA_PATH_PREFILL = 2,         /* query tiles through LDS-staged bf16 MFMA               */
+  PA_PATH_DECODE_BALANCED = 3  /* page-balanced split-K (equal pages per wave) + merge   */
 } pa_path;
 
 /* Host scalars describing one call; everything the planner needs without
@@ -106,9 +107,16 @@ typedef struct pa_plan_info {
 /* Dispatch guard (pure host; reads no device memory).  Picks the route from
  * the query length and the context length, as the attention dispatch guard
  * of the tiny-llm source reading ("Prefill and decode need different
- * kernels") does: max_q_len > 1 -> PA_PATH_PREFILL; otherwise decode, split
- * into S partitions when B*Hkv workgroups would leave the chip's cu_count
- * compute units under-filled and the contexts are long enough to split.
+ * kernels") does: max_q_len > 1 -> PA_PATH_PREFILL.  Decode rows take
+ * PA_PATH_DECODE_BALANCED when B <= 4096 and the contexts can hold at least
+ * one page per wave (B * ceil(max_seq_len / P) >= num_splits): every KV
+ * head's pages, taken in (request, page) order, are cut into num_splits
+ * (= V) equal wave ranges, grid_x = Hkv * V / 4 workgroups (one resident
+ * round: two per compute unit), each wave writes a partial per request it
+ * touches and a merge pass combines them by log-sum-exp.  Otherwise decode
+ * runs one workgroup per (request, KV head), split into S equal partitions
+ * (PA_PATH_DECODE_SPLIT) when B*Hkv workgroups would leave the chip's
+ * cu_count compute units under-filled and the contexts are long enough.
  * cu_count <= 0 means "ask the current device" (falls back to 256). */
 pa_status pa_plan(const pa_desc* desc, int32_t cu_count, pa_plan_info* plan);
 
@@ -120,9 +128,10 @@ size_t pa_workspace_bytes(const pa_desc* desc, int32_t num_splits);
 /* Single-token decode: every request has exactly one query row (n_r = 1, so
  * total_q == B and q_offsets[r] == seq_lens[r] - 1; q_offsets may be NULL).
  * out [B, Hq, d] (dtype), lse float32 [B, Hq] (may be NULL).  The guard may
- * route through split-K, which needs `workspace` of at least
+ * route through a split-K path, which needs `workspace` of at least
  * pa_plan(...).workspace_bytes bytes (else PA_ERR_WORKSPACE); workspace may be
- * NULL when the plan needs none. */
+ * NULL when the plan needs none.  The workspace contents after the call are
+ * internal. */
 pa_status pa_decode(const pa_desc* desc, const void* q, const void* k_pool, const void* v_pool,
                     const int32_t* page_table, const int32_t* seq_lens, const int32_t* q_offsets,
                     float scale, void* out, float* lse, void* workspace, size_t workspace_bytes,

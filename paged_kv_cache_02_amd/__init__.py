@@ -20,9 +20,9 @@ LIB_PATH = os.path.join(HERE, "libpa.so")
 
 PA_OK, PA_ERR_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_METADATA = range(6)
 PA_BF16, PA_F32 = 0, 1
-PA_PATH_DECODE, PA_PATH_DECODE_SPLIT, PA_PATH_PREFILL = 0, 1, 2
+PA_PATH_DECODE, PA_PATH_DECODE_SPLIT, PA_PATH_PREFILL, PA_PATH_DECODE_BALANCED = 0, 1, 2, 3
 PATH_NAMES = {PA_PATH_DECODE: "decode", PA_PATH_DECODE_SPLIT: "decode_split",
-              PA_PATH_PREFILL: "prefill"}
+              PA_PATH_PREFILL: "prefill", PA_PATH_DECODE_BALANCED: "decode_balanced"}
 
 
 class PaError(RuntimeError):
@@ -221,6 +221,44 @@ def pa_prefill_chunk(q, k_pool, v_pool, page_table, seq_lens, q_offsets, scale, 
                                   _ptr(workspace), ws_bytes, _stream(q.device)),
            "pa_prefill_chunk")
     return out, lse
+
+
+class BoundCall:
+    """One library call with its arguments marshalled once, for launch loops
+    in which the per-call Python cost would otherwise starve the GPU queue.
+    It keeps the tensors alive; they must not be reallocated between calls
+    (in-place updates of their contents are fine).  The stream is the current
+    stream at bind time."""
+
+    def __init__(self, name: str, keep, *args):
+        self.name = name
+        self.fn = getattr(lib(), name)
+        self.args = args
+        self.keep = keep
+
+    def __call__(self):
+        _check(self.fn(*self.args), self.name)
+
+
+def bind_decode(q, k_pool, v_pool, page_table, seq_lens, q_offsets, scale, *, out, lse,
+                workspace, desc) -> BoundCall:
+    """pa_decode with fixed arguments (see BoundCall)."""
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    keep = (desc, q, k_pool, v_pool, page_table, seq_lens, q_offsets, out, lse, workspace)
+    return BoundCall("pa_decode", keep, ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                     _ptr(page_table), _ptr(seq_lens), _ptr(q_offsets), float(scale), _ptr(out),
+                     _ptr(lse), _ptr(workspace), ws_bytes, _stream(q.device))
+
+
+def bind_prefill_chunk(q, k_pool, v_pool, page_table, seq_lens, q_offsets, scale, *, q_starts,
+                       out, lse, workspace, desc) -> BoundCall:
+    """pa_prefill_chunk with fixed arguments (see BoundCall)."""
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    keep = (desc, q, k_pool, v_pool, page_table, seq_lens, q_offsets, q_starts, out, lse, workspace)
+    return BoundCall("pa_prefill_chunk", keep, ctypes.byref(desc), _ptr(q), _ptr(k_pool),
+                     _ptr(v_pool), _ptr(page_table), _ptr(seq_lens), _ptr(q_offsets),
+                     _ptr(q_starts), float(scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                     ws_bytes, _stream(q.device))
 
 
 def pa_merge_partials(o_part, lse_part, out_dtype=torch.bfloat16, *, out=None, lse=None):

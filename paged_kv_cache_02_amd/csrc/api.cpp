@@ -17,8 +17,14 @@ namespace {
 // --------------------------------------------------------------------------
 // dispatch-guard tuning constants
 // --------------------------------------------------------------------------
-// Split decode until the grid holds about this many workgroups per CU, so
-// that uneven context lengths still leave every CU busy to the end.
+// Page-balanced decode: resident decode workgroups per CU the grid is sized
+// for (two waves per SIMD, which every decode kernel instance reaches), so
+// the whole grid is one round and all of its waves carry equal page counts.
+constexpr int kDecodeWgsPerCu = 2;
+constexpr int kWavesPerDecodeWg = 4;
+// Fallback equal-split decode (more than pa::kMaxBalancedSeqs requests, or too
+// little work to spread): split until the grid holds about this many
+// workgroups per CU, so that uneven context lengths still leave every CU busy.
 constexpr int kTargetWgsPerCu = 8;
 // A split must keep at least this many pages (4 per wave), or its fixed
 // costs (q load, cross-wave merge, partial write) stop being small.
@@ -122,6 +128,49 @@ pa::DecodeArgs decode_args(const pa_desc* d, const void* q, const void* k_pool, 
   return a;
 }
 
+// Page-balanced decode: V wave ranges per KV head; workspace holds the
+// partials of B + V - 1 slots and the [B, 2] range table.
+int balanced_ranges(const pa_desc* d, int cus) {
+  long long wgs = (long long)cus * kDecodeWgsPerCu / d->num_kv_heads;
+  if (wgs < 1) wgs = 1;
+  if (wgs > (1 << 20)) wgs = 1 << 20;
+  return (int)(wgs * kWavesPerDecodeWg);
+}
+size_t balanced_o_bytes(const pa_desc* d, int V) {
+  return align_up(((size_t)d->num_seqs + V - 1) * d->num_q_heads * d->head_dim * sizeof(float));
+}
+size_t balanced_lse_bytes(const pa_desc* d, int V) {
+  return align_up(((size_t)d->num_seqs + V - 1) * d->num_q_heads * sizeof(float));
+}
+size_t balanced_workspace_bytes(const pa_desc* d, int V) {
+  return balanced_o_bytes(d, V) + balanced_lse_bytes(d, V) +
+         align_up((size_t)d->num_seqs * 2 * sizeof(int32_t));
+}
+
+pa_status run_balanced(const pa_desc* d, pa::DecodeArgs a, int V, void* workspace, void* out,
+                       float* lse, hipStream_t stream) {
+  char* ws = reinterpret_cast<char*>(workspace);
+  a.num_splits = V;
+  a.write_partials = 1;
+  a.o_part = reinterpret_cast<float*>(ws);
+  a.lse_part = reinterpret_cast<float*>(ws + balanced_o_bytes(d, V));
+  a.range_meta = reinterpret_cast<int32_t*>(ws + balanced_o_bytes(d, V) + balanced_lse_bytes(d, V));
+  const int G = d->num_q_heads / d->num_kv_heads;
+  if (pa::launch_decode_balanced(a, d->dtype, d->head_dim, G, stream) != hipSuccess)
+    return PA_ERR_HIP;
+  pa::MergeArgs m;
+  m.o_part = a.o_part;
+  m.lse_part = a.lse_part;
+  m.range_meta = a.range_meta;
+  m.out = out;
+  m.lse = lse;
+  m.rows = d->num_seqs;
+  m.heads = d->num_q_heads;
+  m.num_splits = V;
+  if (pa::launch_merge(m, d->dtype, d->head_dim, stream) != hipSuccess) return PA_ERR_HIP;
+  return PA_OK;
+}
+
 // Split launch + merge launch shared by pa_decode (guard-chosen S) and
 // pa_split_merge (caller-chosen S).
 pa_status run_split(const pa_desc* d, pa::DecodeArgs a, int S, void* workspace, void* out,
@@ -137,6 +186,7 @@ pa_status run_split(const pa_desc* d, pa::DecodeArgs a, int S, void* workspace, 
   pa::MergeArgs m;
   m.o_part = o_part;
   m.lse_part = lse_part;
+  m.range_meta = nullptr;
   m.out = out;
   m.lse = lse;
   m.rows = d->num_seqs;
@@ -236,6 +286,14 @@ pa_status pa_plan(const pa_desc* d, int32_t cu_count, pa_plan_info* plan) {
   if (!pa::decode_group_supported(G)) return PA_ERR_UNSUPPORTED;
   const long long units = (long long)d->num_seqs * d->num_kv_heads;
   const int max_pages = (d->max_seq_len + d->page_size - 1) / d->page_size;
+  const int V = balanced_ranges(d, cus);
+  if (d->num_seqs <= pa::kMaxBalancedSeqs && (long long)d->num_seqs * max_pages >= V) {
+    plan->path = PA_PATH_DECODE_BALANCED;
+    plan->num_splits = V;
+    plan->grid_x = (int32_t)((long long)d->num_kv_heads * (V / kWavesPerDecodeWg));
+    plan->workspace_bytes = balanced_workspace_bytes(d, V);
+    return PA_OK;
+  }
   const long long target = (long long)kTargetWgsPerCu * cus;
   int S = 1;
   if (units > 0 && units < target) {
@@ -264,6 +322,11 @@ pa_status pa_decode(const pa_desc* d, const void* q, const void* k_pool, const v
   if (st != PA_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   pa::DecodeArgs a = decode_args(d, q, k_pool, v_pool, page_table, seq_lens, scale);
+  if (plan.path == PA_PATH_DECODE_BALANCED) {
+    if (workspace == nullptr || workspace_bytes < plan.workspace_bytes || !aligned16(workspace))
+      return PA_ERR_WORKSPACE;
+    return run_balanced(d, a, plan.num_splits, workspace, out, lse, s);
+  }
   if (plan.num_splits == 1) {
     a.out = out;
     a.lse = lse;
@@ -362,6 +425,7 @@ pa_status pa_merge_partials(int32_t rows, int32_t heads, int32_t num_splits, int
   pa::MergeArgs m;
   m.o_part = o_part;
   m.lse_part = lse_part;
+  m.range_meta = nullptr;
   m.out = out;
   m.lse = lse;
   m.rows = rows;

@@ -49,7 +49,8 @@ template <typename T, int D, int G>
 struct Shape {
   static constexpr int kVec = 16 / (int)sizeof(T);   // elements per 16-byte chunk
   static constexpr int kChunks = D / kVec;            // chunks per key row
-  static constexpr int kLptMin = (G * D + 63) / 64;   // accumulator <= 64 floats
+  static constexpr int kAccMax = 32;                  // accumulator floats per lane
+  static constexpr int kLptMin = (G * D + kAccMax - 1) / kAccMax;
   static constexpr int kLpt0 = kLptMin <= 4 ? 4 : (kLptMin <= 8 ? 8 : 16);
   static constexpr int kLpt = kLpt0 > kChunks ? kChunks : kLpt0;  // lanes per key row
   static constexpr int kRowsPerLoad = 64 / kLpt;      // key rows per wave load
@@ -140,19 +141,31 @@ struct Half {  // the K (or V) registers of one (page, KV head) block
 
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
-// Issue the loads of one K or V block (16 keys x d, contiguous).  Every K/V
-// byte is read exactly once, so the loads are marked nontemporal (streamed
-// past the caches), which sustains a higher HBM read rate.
+// Buffer resource word 3 for gfx9-family raw (unstructured) buffers.
+constexpr int kBufferWord3 = 0x00020000;
+// Cache-policy bits of a buffer load: nontemporal (streamed past the caches).
+constexpr int kLoadNontemporal = 2;
+
+// Issue the loads of one K or V block (16 keys x d, contiguous) through a
+// raw buffer resource that covers exactly that block.  Every K/V byte is read
+// once, so the loads are nontemporal.  A resource with zero records makes
+// every load of the block return zeros without touching memory, which lets
+// the software pipeline issue its lookahead loads unconditionally (the
+// wait counts the compiler inserts then stay exact across iterations).
 template <typename T, int D, int G>
-__device__ __forceinline__ void load_half(Half<T, D, G>& hr, const T* __restrict__ blk, int row0,
+__device__ __forceinline__ void load_half(Half<T, D, G>& hr, const T* blk, bool live, int row0,
                                           int col) {
   using S = Shape<T, D, G>;
+  const int bytes = live ? kPageSize * D * (int)sizeof(T) : 0;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(blk), (short)0, bytes, kBufferWord3);
 #pragma unroll
   for (int kk = 0; kk < S::kKeysPerLane; ++kk) {
 #pragma unroll
     for (int jj = 0; jj < S::kChunksPerLane; ++jj) {
       const int off = (row0 + S::kRowsPerLoad * kk) * D + (col + S::kLpt * jj) * S::kVec;
-      const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(blk + off));
+      const u32x4_t v =
+          __builtin_amdgcn_raw_buffer_load_b128(rs, off * (int)sizeof(T), 0, kLoadNontemporal);
       hr.c[kk][jj] = make_uint4(v[0], v[1], v[2], v[3]);
     }
   }
@@ -252,47 +265,8 @@ __device__ __forceinline__ void page_values(const Half<T, D, G>& vr, WaveState<T
 }
 
 template <typename T, int D, int G>
-__global__ void __launch_bounds__(kThreads)
-decode_kernel(DecodeArgs a) {
+__device__ __forceinline__ void reset_state(WaveState<T, D, G>& st) {
   using S = Shape<T, D, G>;
-  const int32_t num_pages = a.num_pages;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int col = lane % S::kLpt;
-  const int row0 = lane / S::kLpt;
-
-  const int nsplit = a.num_splits;
-  const int bid = blockIdx.x;
-  const int split = bid % nsplit;
-  const int rg = bid / nsplit;
-  const int g = rg % a.num_kv_heads;
-  const int r = rg / a.num_kv_heads;
-  const int Hq = a.num_q_heads;
-  const int Hkv = a.num_kv_heads;
-
-  const int L = a.seq_lens[r];
-  int npages = (L + kPageSize - 1) / kPageSize;
-  npages = npages < a.max_pages_per_seq ? npages : a.max_pages_per_seq;
-  const int pps = (npages + nsplit - 1) / nsplit;
-  const int pb = split * pps;
-  const int pe = (pb + pps) < npages ? (pb + pps) : npages;
-
-  const T* __restrict__ qp = reinterpret_cast<const T*>(a.q);
-  const T* __restrict__ kpool = reinterpret_cast<const T*>(a.k_pool);
-  const T* __restrict__ vpool = reinterpret_cast<const T*>(a.v_pool);
-  const int32_t* __restrict__ ptab = a.page_table + (size_t)r * a.max_pages_per_seq;
-
-  // q chunks of the lane's dims for every head of the group
-  uint4 qv[G][S::kChunksPerLane];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const T* qrow = qp + ((size_t)r * Hq + (size_t)g * G + h) * D;
-#pragma unroll
-    for (int jj = 0; jj < S::kChunksPerLane; ++jj)
-      qv[h][jj] = *reinterpret_cast<const uint4*>(qrow + (col + S::kLpt * jj) * S::kVec);
-  }
-
-  WaveState<T, D, G> st;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     st.m[h] = -INFINITY;
@@ -300,47 +274,14 @@ decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int e = 0; e < S::kDimsPerLane; ++e) st.acc[h][e] = 0.f;
   }
+}
 
-  const size_t blk = (size_t)kPageSize * D;  // elements of one (page, head) block
-  auto block_of = [&](int pg) -> size_t {
-    int phys = ptab[pg];
-    phys = phys < 0 ? 0 : (phys >= num_pages ? num_pages - 1 : phys);
-    return ((size_t)phys * Hkv + g) * blk;
-  };
-
-  // Staggered software pipeline over the wave's pages p, p+4, p+8, ...:
-  // K of the next page is requested before the current page's scores, V of
-  // the next page before the current page's value update, so each load has a
-  // full half-iteration of work in front of it while at most one extra block
-  // of K and one of V are held in registers.
-  int p = pb + wave;
-  if (p < pe) {
-    Half<T, D, G> kc, kn, vc, vn;
-    size_t off = block_of(p);
-    load_half<T, D, G>(kc, kpool + off, row0, col);
-    load_half<T, D, G>(vc, vpool + off, row0, col);
-#pragma unroll 1
-    for (;;) {
-      const int pn = p + kWaves;
-      const bool more = pn < pe;
-      size_t offn = 0;
-      if (more) {
-        offn = block_of(pn);
-        load_half<T, D, G>(kn, kpool + offn, row0, col);
-      }
-      const int live = L - p * kPageSize;  // >= 16 except on the last page
-      float pr[S::kKeysPerLane][G];
-      page_scores<T, D, G>(kc, qv, st, live, row0, a.scale_log2, pr);
-      if (more) load_half<T, D, G>(vn, vpool + offn, row0, col);
-      page_values<T, D, G>(vc, st, live, row0, pr);
-      if (!more) break;
-      kc = kn;
-      vc = vn;
-      p = pn;
-    }
-  }
-
-  // ---- merge the wave's lanes that hold different keys of the same dims ----
+// Combine the wave's lanes that hold different keys of the same dims (the
+// lanes that differ in row0): afterwards every lane holds the wave's total
+// m, l and acc for its dims, by the log-sum-exp rule.
+template <typename T, int D, int G>
+__device__ __forceinline__ void wave_combine(WaveState<T, D, G>& st) {
+  using S = Shape<T, D, G>;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     float M = st.m[h];
@@ -360,6 +301,145 @@ decode_kernel(DecodeArgs a) {
       st.acc[h][e] = v;
     }
   }
+}
+
+// q chunks of the lane's dims for the G query heads of KV head g of request
+// r, through a buffer resource; valid = false gives zeros and reads nothing.
+template <typename T, int D, int G>
+using QRegs = uint4[G][Shape<T, D, G>::kChunksPerLane];
+
+template <typename T, int D, int G>
+__device__ __forceinline__ void load_q(QRegs<T, D, G>& qv, const T* q, int Hq, int r, int g,
+                                       bool valid, int col) {
+  using S = Shape<T, D, G>;
+  const T* base = q + ((size_t)r * Hq + (size_t)g * G) * D;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T*>(base), (short)0, valid ? G * D * (int)sizeof(T) : 0, kBufferWord3);
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+#pragma unroll
+    for (int jj = 0; jj < S::kChunksPerLane; ++jj) {
+      const int off = h * D + (col + S::kLpt * jj) * S::kVec;
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, off * (int)sizeof(T), 0, 0);
+      qv[h][jj] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+  }
+}
+
+// Depth of the K/V software pipeline: while page i is scored and accumulated,
+// the K and V blocks of pages i+1 .. i+kDepth are in flight.  The depth is
+// the largest (up to 4) whose buffers still leave room for two waves per
+// SIMD: accumulator + q (+ kExtraRegs) + scores/probabilities + 2 (depth + 1)
+// K/V buffers within 224 VGPRs.
+template <typename T, int D, int G, int kExtraRegs>
+struct Pipe {
+  using S = Shape<T, D, G>;
+  static constexpr int kHalfRegs = (int)(sizeof(Half<T, D, G>) / 4);
+  static constexpr int kFixedRegs = G * S::kDimsPerLane + G * S::kChunksPerLane * 4 +
+                                    2 * G * S::kKeysPerLane + kExtraRegs;
+  static constexpr int kDepth = kFixedRegs + 10 * kHalfRegs <= 224  ? 4
+                                : kFixedRegs + 8 * kHalfRegs <= 224 ? 3
+                                : kFixedRegs + 6 * kHalfRegs <= 224 ? 2
+                                                                    : 1;
+  static constexpr int kBufs = kDepth + 1;
+};
+
+template <typename T, int D, int G>
+__global__ void __launch_bounds__(kThreads)
+decode_kernel(DecodeArgs a) {
+  using S = Shape<T, D, G>;
+  const int32_t num_pages = a.num_pages;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane % S::kLpt;
+  const int row0 = lane / S::kLpt;
+
+  const int nsplit = a.num_splits;
+  const int bid = blockIdx.x;
+  // the KV heads of one (request, split) are adjacent workgroups: they read
+  // neighbouring blocks of the same pages at about the same time
+  const int g = bid % a.num_kv_heads;
+  const int rs = bid / a.num_kv_heads;
+  const int split = rs % nsplit;
+  const int r = rs / nsplit;
+  const int Hq = a.num_q_heads;
+  const int Hkv = a.num_kv_heads;
+
+  const int L = a.seq_lens[r];
+  int npages = (L + kPageSize - 1) / kPageSize;
+  npages = npages < a.max_pages_per_seq ? npages : a.max_pages_per_seq;
+  const int pps = (npages + nsplit - 1) / nsplit;
+  const int pb = split * pps;
+  const int pe = (pb + pps) < npages ? (pb + pps) : npages;
+
+  const T* __restrict__ qp = reinterpret_cast<const T*>(a.q);
+  const T* __restrict__ kpool = reinterpret_cast<const T*>(a.k_pool);
+  const T* __restrict__ vpool = reinterpret_cast<const T*>(a.v_pool);
+  const int32_t* __restrict__ ptab = a.page_table + (size_t)r * a.max_pages_per_seq;
+
+  // q chunks of the lane's dims for every head of the group
+  uint4 qv[G][S::kChunksPerLane];
+  load_q<T, D, G>(qv, qp, Hq, r, g, true, col);
+
+  WaveState<T, D, G> st;
+  reset_state<T, D, G>(st);
+
+  const size_t blk = (size_t)kPageSize * D;  // elements of one (page, head) block
+
+  // The wave's pages are pb + wave + kWaves * i for i in [0, nw).  The
+  // physical id of the page whose loads are issued next is fetched one step
+  // earlier (a uniform, scalar load), so its latency is hidden behind a page
+  // of work.
+  const int first = pb + wave;
+  const int nw = first < pe ? (pe - first + kWaves - 1) / kWaves : 0;
+  auto page_id = [&](int i) -> int {  // clamped index: always a valid entry
+    const int ic = i < nw ? i : nw - 1;
+    int phys = ptab[first + kWaves * ic];
+    return phys < 0 ? 0 : (phys >= num_pages ? num_pages - 1 : phys);
+  };
+  auto block_ptr = [&](const T* pool, int phys) -> const T* {
+    return pool + ((size_t)phys * Hkv + g) * blk;
+  };
+
+  // Software pipeline Pipe::kDepth pages deep.  K of page i+kDepth is
+  // requested before page i's scores and its V before page i's value update.
+  // The kDepth+1 register buffers rotate through a fully unrolled inner loop,
+  // so no buffer is ever copied.  Lookahead pages past the wave's last one
+  // are loaded with zero-record resources.
+  constexpr int kDepth = Pipe<T, D, G, 0>::kDepth;
+  constexpr int kBufs = Pipe<T, D, G, 0>::kBufs;
+  if (nw > 0) {
+    Half<T, D, G> hk[kBufs], hv[kBufs];
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u) {
+      const int phys = page_id(u);
+      load_half<T, D, G>(hk[u], block_ptr(kpool, phys), u < nw, row0, col);
+      load_half<T, D, G>(hv[u], block_ptr(vpool, phys), u < nw, row0, col);
+    }
+    int next_phys = page_id(kDepth);
+    int i = 0;
+#pragma unroll 1
+    for (;;) {
+#pragma unroll
+      for (int u = 0; u < kBufs; ++u) {
+        const int ahead = i + kDepth;
+        const bool more = ahead < nw;
+        const int nb = (u + kDepth) % kBufs;  // buffer of page i + kDepth
+        const int phys = next_phys;
+        load_half<T, D, G>(hk[nb], block_ptr(kpool, phys), more, row0, col);
+        next_phys = page_id(ahead + 1);
+        const int live = L - (first + kWaves * i) * kPageSize;  // >= 16 except on the last page
+        float pr[S::kKeysPerLane][G];
+        page_scores<T, D, G>(hk[u], qv, st, live, row0, a.scale_log2, pr);
+        load_half<T, D, G>(hv[nb], block_ptr(vpool, phys), more, row0, col);
+        page_values<T, D, G>(hv[u], st, live, row0, pr);
+        if (++i >= nw) goto pages_done;
+      }
+    }
+  }
+pages_done:
+
+  wave_combine<T, D, G>(st);
 
   // ---- merge the waves through LDS ----
   __shared__ float sm_m[kWaves][G];
@@ -411,6 +491,254 @@ decode_kernel(DecodeArgs a) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Page-balanced split-K decode.
+//
+// The pages of all requests, taken in (request, page) order, form one
+// sequence per KV head; it is cut into V equal contiguous wave ranges and
+// every wave of the grid owns one range of one KV head, so all waves carry
+// the same load whatever the mix of context lengths, and the grid is a
+// single round of resident workgroups.  A wave's range can end inside a
+// request and can span several requests: at every request boundary (and at
+// the range end) the wave writes its normalized partial output and lse for
+// that request, and the merge pass combines the partials of each request by
+// the log-sum-exp rule (the same combine as split-K; Flash-Decoding, adv04
+// of the mini-vllm-tutorial advanced series).
+//
+// Partial slots: along a KV head's sequence both the request index r and the
+// wave-range index v only grow, and one of them grows at every change of the
+// pair (r, v), so slot r + v is unique per pair; B + V - 1 slots suffice.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int pages_of(int L, int max_pages) {
+  if (L <= 0) return 0;
+  const int p = (L + kPageSize - 1) / kPageSize;
+  return p < max_pages ? p : max_pages;
+}
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// pre[r] = pages of requests 0 .. r-1 for r in [0, B] (whole workgroup; ends
+// with a barrier).
+__device__ void page_prefix(int* pre, const int32_t* __restrict__ seq_lens, int B, int max_pages) {
+  __shared__ int wave_tot[kWaves];
+  const int t = threadIdx.x;
+  const int per = (B + kThreads - 1) / kThreads;
+  const int r0 = t * per;
+  int local = 0;
+  for (int k = 0; k < per; ++k)
+    if (r0 + k < B) local += pages_of(seq_lens[r0 + k], max_pages);
+  int x = local;  // inclusive scan over the wave
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if ((t & 63) >= o) x += y;
+  }
+  if ((t & 63) == 63) wave_tot[t >> 6] = x;
+  __syncthreads();
+  int run = x - local;
+  for (int w = 0; w < (t >> 6); ++w) run += wave_tot[w];
+  if (t == 0) pre[0] = 0;
+  for (int k = 0; k < per; ++k) {
+    if (r0 + k < B) {
+      run += pages_of(seq_lens[r0 + k], max_pages);
+      pre[r0 + k + 1] = run;
+    }
+  }
+  __syncthreads();
+}
+
+// The metadata and the partial outputs come as separate restrict parameters:
+// with them the compiler can prove that the kernel's own stores never touch
+// the page table, and reads page ids with scalar loads (a vector load there
+// would make each wait for a page id also wait for every K/V load in flight).
+template <typename T, int D, int G>
+__global__ void __launch_bounds__(kThreads)
+decode_balanced_kernel(DecodeArgs a, const int32_t* __restrict__ page_table,
+                       const int32_t* __restrict__ seq_lens, float* __restrict__ o_part,
+                       float* __restrict__ lse_part, int32_t* __restrict__ range_meta) {
+  using S = Shape<T, D, G>;
+  // the prefetched q of the next request costs one more q register set
+  using P = Pipe<T, D, G, G * S::kChunksPerLane * 4>;
+  constexpr int kDepth = P::kDepth;
+  constexpr int kBufs = P::kBufs;
+  __shared__ int pre[kMaxBalancedSeqs + 1];
+
+  const int32_t num_pages = a.num_pages;
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int col = lane % S::kLpt;
+  const int row0 = lane / S::kLpt;
+  const int Hq = a.num_q_heads;
+  const int Hkv = a.num_kv_heads;
+  const int B = a.num_seqs;
+  const int maxp = a.max_pages_per_seq;
+  const int V = a.num_splits;
+  const int g = blockIdx.x % Hkv;
+  const int v = (blockIdx.x / Hkv) * kWaves + wave;
+
+  page_prefix(pre, seq_lens, B, maxp);
+  const int N = uniform(pre[B]);
+  const int per = N > 0 ? (N + V - 1) / V : 1;  // pages per wave range
+
+  // one workgroup records which wave ranges each request spans
+  if (blockIdx.x == 0) {
+    for (int r = threadIdx.x; r < B; r += kThreads) {
+      const int s0 = pre[r], s1 = pre[r + 1];
+      range_meta[2 * r] = s0 < s1 ? s0 / per : 0;
+      range_meta[2 * r + 1] = s0 < s1 ? (s1 - 1) / per : -1;
+    }
+  }
+
+  const long long f0l = (long long)v * per;
+  if (f0l >= N) return;
+  const int f0 = (int)f0l;
+  const int nw = (f0 + per < N ? f0 + per : N) - f0;  // pages of this wave, >= 1
+
+  auto npages = [&](int r) -> int { return uniform(pre[r + 1]) - uniform(pre[r]); };
+  // the first request after r that owns pages (B if none)
+  auto next_req = [&](int r) -> int {
+    ++r;
+    while (r < B && npages(r) == 0) ++r;
+    return r;
+  };
+  auto seq_len = [&](int r) -> int {
+    const int L = seq_lens[r];
+    return L < maxp * kPageSize ? L : maxp * kPageSize;
+  };
+
+  // request holding page f0: the largest r with pre[r] <= f0
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (uniform(pre[mid]) <= f0) lo = mid;
+    else hi = mid - 1;
+  }
+
+  const T* __restrict__ qp = reinterpret_cast<const T*>(a.q);
+  const T* __restrict__ kpool = reinterpret_cast<const T*>(a.k_pool);
+  const T* __restrict__ vpool = reinterpret_cast<const T*>(a.v_pool);
+  const size_t blk = (size_t)kPageSize * D;
+  auto block_ptr = [&](const T* pool, int phys) -> const T* {
+    return pool + ((size_t)phys * Hkv + g) * blk;
+  };
+
+  // load cursor (request rl, page jl of it, its page count nl): the page
+  // whose K/V loads are issued next
+  int rl = lo, jl = f0 - uniform(pre[lo]), nl = npages(lo);
+  auto advance_load = [&]() {
+    ++jl;
+    while (jl >= nl && rl + 1 < B) {
+      ++rl;
+      jl = 0;
+      nl = npages(rl);
+    }
+  };
+  auto load_id = [&]() -> int {
+    int phys = page_table[(size_t)rl * maxp + jl];
+    return phys < 0 ? 0 : (phys >= num_pages ? num_pages - 1 : phys);
+  };
+
+  // compute cursor
+  int rc = lo, jc = f0 - uniform(pre[lo]), nc = npages(lo);
+  int Lc = seq_len(rc);
+
+  uint4 qv[G][S::kChunksPerLane], qn[G][S::kChunksPerLane];
+  load_q<T, D, G>(qv, qp, Hq, rc, g, true, col);
+  int rq = next_req(rc);  // request whose q sits in qn
+  load_q<T, D, G>(qn, qp, Hq, rq < B ? rq : B - 1, g, rq < B && uniform(pre[rq]) < f0 + nw, col);
+
+  WaveState<T, D, G> st;
+  reset_state<T, D, G>(st);
+
+  Half<T, D, G> hk[kBufs], hv[kBufs];
+#pragma unroll
+  for (int u = 0; u < kDepth; ++u) {
+    const int phys = load_id();
+    load_half<T, D, G>(hk[u], block_ptr(kpool, phys), u < nw, row0, col);
+    load_half<T, D, G>(hv[u], block_ptr(vpool, phys), u < nw, row0, col);
+    if (u + 1 < nw) advance_load();
+  }
+  int next_phys = load_id();
+
+  int i = 0;
+#pragma unroll 1
+  for (;;) {
+#pragma unroll
+    for (int u = 0; u < kBufs; ++u) {
+      const int ahead = i + kDepth;
+      const bool more = ahead < nw;
+      const int nb = (u + kDepth) % kBufs;  // buffer of page i + kDepth
+      const int phys = next_phys;
+      load_half<T, D, G>(hk[nb], block_ptr(kpool, phys), more, row0, col);
+      if (ahead + 1 < nw) advance_load();
+      next_phys = load_id();
+      const int live = Lc - jc * kPageSize;  // >= 16 except on a request's last page
+      float pr[S::kKeysPerLane][G];
+      page_scores<T, D, G>(hk[u], qv, st, live, row0, a.scale_log2, pr);
+      load_half<T, D, G>(hv[nb], block_ptr(vpool, phys), more, row0, col);
+      page_values<T, D, G>(hv[u], st, live, row0, pr);
+
+      const bool range_end = i + 1 >= nw;
+      if (jc + 1 >= nc || range_end) {
+        // ---- the wave's share of request rc is complete: write its partial
+        wave_combine<T, D, G>(st);
+        if (row0 == 0) {
+          const size_t slot = (size_t)rc + v;
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const int hq = g * G + h;
+            const float l = st.l[h];
+            const bool empty = !(l > 0.f);
+            const float inv = empty ? 0.f : 1.f / l;
+            float* o = o_part + (slot * Hq + hq) * D;
+#pragma unroll
+            for (int jj = 0; jj < S::kChunksPerLane; ++jj) {
+#pragma unroll
+              for (int e = 0; e < S::kVec; e += 4) {
+                float4 w;
+                w.x = st.acc[h][jj * S::kVec + e + 0] * inv;
+                w.y = st.acc[h][jj * S::kVec + e + 1] * inv;
+                w.z = st.acc[h][jj * S::kVec + e + 2] * inv;
+                w.w = st.acc[h][jj * S::kVec + e + 3] * inv;
+                *reinterpret_cast<float4*>(o + (col + S::kLpt * jj) * S::kVec + e) = w;
+              }
+            }
+            if (col == 0) lse_part[slot * Hq + hq] = empty ? -INFINITY : (st.m[h] + __log2f(l)) * kLn2;
+          }
+        }
+        if (range_end) return;
+        reset_state<T, D, G>(st);
+        // ---- move on to the next request of the range
+        rc = rq;
+        jc = 0;
+        nc = npages(rc);
+        Lc = seq_len(rc);
+        // The copy must complete before the next q load is issued, so that the
+        // load can land in the registers qn already occupies (a load into
+        // temporaries followed by a copy would wait for every load in flight):
+        // the empty asm reads the copied registers and orders memory.
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+#pragma unroll
+          for (int jj = 0; jj < S::kChunksPerLane; ++jj) {
+            qv[h][jj] = qn[h][jj];
+            asm volatile("" : "+v"(qv[h][jj].x), "+v"(qv[h][jj].y), "+v"(qv[h][jj].z),
+                         "+v"(qv[h][jj].w)::"memory");
+          }
+        }
+        rq = next_req(rc);
+        load_q<T, D, G>(qn, qp, Hq, rq < B ? rq : B - 1, g, rq < B && uniform(pre[rq]) < f0 + nw,
+                        col);
+      } else {
+        ++jc;
+      }
+      ++i;
+    }
+  }
+}
+
 template <typename T, int D, int G>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
   const long long grid = (long long)a.num_seqs * a.num_kv_heads * a.num_splits;
@@ -418,6 +746,28 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((decode_kernel<T, D, G>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
+}
+
+template <typename T, int D, int G>
+hipError_t launch_bal_t(const DecodeArgs& a, hipStream_t s) {
+  const long long grid = (long long)a.num_kv_heads * (a.num_splits / kWaves);
+  if (grid <= 0 || a.num_seqs <= 0) return hipSuccess;
+  if (grid > 0x7FFFFFFFLL || a.num_splits % kWaves != 0 || a.num_seqs > kMaxBalancedSeqs)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL((decode_balanced_kernel<T, D, G>), dim3((unsigned)grid), dim3(kThreads), 0, s,
+                     a, a.page_table, a.seq_lens, a.o_part, a.lse_part, a.range_meta);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_bal_g(const DecodeArgs& a, int group, hipStream_t s) {
+  switch (group) {
+    case 1: return launch_bal_t<T, D, 1>(a, s);
+    case 2: return launch_bal_t<T, D, 2>(a, s);
+    case 4: return launch_bal_t<T, D, 4>(a, s);
+    case 8: return launch_bal_t<T, D, 8>(a, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <typename T, int D>
@@ -435,6 +785,18 @@ hipError_t launch_g(const DecodeArgs& a, int group, hipStream_t s) {
 
 bool decode_group_supported(int group) {
   return group == 1 || group == 2 || group == 4 || group == 8;
+}
+
+hipError_t launch_decode_balanced(const DecodeArgs& a, int dtype, int head_dim, int group,
+                                  hipStream_t s) {
+  if (dtype == 0) {
+    if (head_dim == 128) return launch_bal_g<__bf16, 128>(a, group, s);
+    if (head_dim == 64) return launch_bal_g<__bf16, 64>(a, group, s);
+  } else if (dtype == 1) {
+    if (head_dim == 128) return launch_bal_g<float, 128>(a, group, s);
+    if (head_dim == 64) return launch_bal_g<float, 64>(a, group, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int group, hipStream_t s) {

@@ -9,7 +9,9 @@
 //
 // One wave per (row, head): lanes read the S partial lse values (strided by
 // 64), reduce max and sum with wave shuffles, then each lane produces d/64 of
-// the output dims, reading the S partial rows coalesced.
+// the output dims, reading the S partial rows coalesced.  Partials come
+// either S per (row, head) (equal splits) or as a variable run of slots per
+// row given by a range table (page-balanced splits).
 #include "pa_internal.h"
 
 #include <math.h>
@@ -45,17 +47,31 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) merge_kernel(MergeArgs a)
   const long long rh = (long long)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   const long long nrh = (long long)a.rows * a.heads;
   if (rh >= nrh) return;
-  const int S = a.num_splits;
-  const float* lp = a.lse_part + rh * S;
-  const float* op = a.o_part + rh * S * D;
+  // partial s of this (row, head) is row  base + s * step  of the partial arrays
+  long long base, step;
+  int S;
+  if (a.range_meta == nullptr) {
+    S = a.num_splits;
+    base = rh * S;
+    step = 1;
+  } else {
+    const long long r = rh / a.heads;
+    const int first = a.range_meta[2 * r];
+    const int last = a.range_meta[2 * r + 1];
+    S = last >= first ? last - first + 1 : 0;
+    base = (r + first) * a.heads + rh % a.heads;
+    step = a.heads;
+  }
+  const float* lp = a.lse_part;
+  const float* op = a.o_part;
 
   float M = -INFINITY;
-  for (int s = lane; s < S; s += 64) M = fmaxf(M, lp[s]);
+  for (int s = lane; s < S; s += 64) M = fmaxf(M, lp[base + s * step]);
   M = wave_max(M);
   const float Mb = (M == -INFINITY) ? 0.f : M;   // all splits empty: weights stay 0
   float tot = 0.f;
   for (int s = lane; s < S; s += 64) {
-    const float v = lp[s];
+    const float v = lp[base + s * step];
     tot += (v == -INFINITY) ? 0.f : exp2f((v - Mb) * kLog2e);
   }
   tot = wave_sum(tot);
@@ -68,10 +84,11 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) merge_kernel(MergeArgs a)
   for (int i = 0; i < kPer; ++i) acc[i] = 0.f;
   if (!empty) {
     for (int s = 0; s < S; ++s) {
-      const float v = lp[s];
+      const long long row = base + s * step;
+      const float v = lp[row];
       const float w = (v == -INFINITY) ? 0.f : exp2f((v - LSE) * kLog2e);
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) acc[i] = fmaf(w, op[(long long)s * D + lane + 64 * i], acc[i]);
+      for (int i = 0; i < kPer; ++i) acc[i] = fmaf(w, op[row * D + lane + 64 * i], acc[i]);
     }
   }
   T* out = reinterpret_cast<T*>(a.out) + rh * D;

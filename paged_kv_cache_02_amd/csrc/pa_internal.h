@@ -11,6 +11,9 @@
 namespace pa {
 
 constexpr int kPageSize = 16;  // keys per page (the only page size built)
+// Requests the page-balanced decode handles in one call (its per-request page
+// prefix lives in LDS).
+constexpr int kMaxBalancedSeqs = 4096;
 
 // ---------------------------------------------------------------------------
 // decode / split-K partition kernel
@@ -23,11 +26,12 @@ struct DecodeArgs {
   const int32_t* seq_lens;    // [B]
   void* out;                // [B, Hq, d]     (unsplit)
   float* lse;               // [B, Hq] or null (unsplit)
-  float* o_part;            // [B, Hq, S, d]  (split)
-  float* lse_part;          // [B, Hq, S]     (split)
+  float* o_part;            // [B, Hq, S, d] (split) or [B + V - 1, Hq, d] (balanced)
+  float* lse_part;          // [B, Hq, S]    (split) or [B + V - 1, Hq]    (balanced)
+  int32_t* range_meta;      // balanced: [B, 2] first and last wave range of each request
   int32_t num_seqs, num_q_heads, num_kv_heads, max_pages_per_seq;
   int32_t num_pages;        // pool size; page ids are clamped into [0, num_pages)
-  int32_t num_splits;       // S partitions per (request, KV head)
+  int32_t num_splits;       // S partitions per (request, KV head); balanced: V wave ranges
   int32_t write_partials;   // 1: write o_part/lse_part; 0: write out/lse (needs S == 1)
   float scale_log2;         // scale * log2(e)
 };
@@ -35,13 +39,20 @@ struct DecodeArgs {
 // dtype: 0 = bf16, 1 = fp32.  Returns hipSuccess or the launch error.
 bool decode_group_supported(int group);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int group, hipStream_t s);
+// Page-balanced split: every KV head's flattened (request, page) sequence is
+// cut into a.num_splits equal wave ranges (a.num_splits a multiple of 4).
+hipError_t launch_decode_balanced(const DecodeArgs& a, int dtype, int head_dim, int group,
+                                  hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // log-sum-exp merge of split partials
 // ---------------------------------------------------------------------------
 struct MergeArgs {
-  const float* o_part;      // [rows, heads, S, d]
-  const float* lse_part;    // [rows, heads, S]
+  const float* o_part;      // [rows, heads, S, d], or [rows + S - 1, heads, d] with range_meta
+  const float* lse_part;    // [rows, heads, S],    or [rows + S - 1, heads]
+  // null: fixed S partials per (row, head).  Otherwise [rows, 2]: row r's
+  // partials sit in slots r + v for v in [meta[2r], meta[2r+1]].
+  const int32_t* range_meta;
   void* out;                // [rows, heads, d]
   float* lse;               // [rows, heads] or null
   int32_t rows, heads, num_splits;

@@ -41,22 +41,44 @@ def test_plan_routes_by_query_length():
     info = pa.pa_plan(desc(max_q_len=512, total_q=2048), cu_count=256)
     assert info["path"] == "prefill" and info["workspace_bytes"] == 0
     info = pa.pa_plan(desc(), cu_count=256)
-    assert info["path"] in ("decode", "decode_split")
+    assert info["path"] == "decode_balanced"
 
 
-def test_plan_splits_only_when_the_grid_is_small():
-    # 64 x 8 = 512 units at 8K context on 256 CUs -> split
+def align256(x):
+    return (x + 255) // 256 * 256
+
+
+def test_plan_balanced_decode_sizes_one_round_of_waves():
+    # 2 workgroups of 4 waves per CU, shared evenly by the KV heads
     d3 = desc(B=64, Hq=32, Hkv=8, NP=20000, MP=512, max_seq_len=8192)
     p3 = pa.pa_plan(d3, cu_count=256)
-    assert p3["path"] == "decode_split" and p3["num_splits"] > 1
-    assert p3["workspace_bytes"] == pa.pa_workspace_bytes(d3, p3["num_splits"])
-    assert p3["grid_x"] == 64 * 8 * p3["num_splits"]
-    # plenty of units already -> no split
-    big = desc(B=1024, Hq=32, Hkv=8, NP=70000, MP=64, max_seq_len=1024)
+    V = 4 * (2 * 256 // 8)
+    assert p3["path"] == "decode_balanced" and p3["num_splits"] == V
+    assert p3["grid_x"] == 8 * V // 4 == 2 * 256
+    slots = 64 + V - 1
+    assert p3["workspace_bytes"] == (align256(slots * 32 * 128 * 4) + align256(slots * 32 * 4) +
+                                     align256(64 * 2 * 4))
+    # more KV heads than workgroup slots: one workgroup (4 wave ranges) per head
+    many = desc(B=8, Hq=1024, Hkv=1024, NP=5000, MP=512, max_seq_len=8192)
+    pm = pa.pa_plan(many, cu_count=256)
+    assert pm["path"] == "decode_balanced" and pm["num_splits"] == 4 and pm["grid_x"] == 1024
+
+
+def test_plan_falls_back_to_equal_splits():
+    # past the balanced request limit, plenty of units -> one workgroup each
+    big = desc(B=5000, Hq=32, Hkv=8, NP=400000, MP=64, max_seq_len=1024)
     assert pa.pa_plan(big, cu_count=256)["path"] == "decode"
-    # short contexts cannot be split below the minimum split length
+    # too few pages to give every wave one -> the equal-split route, which
+    # cannot split below its minimum split length either
     short = desc(B=4, Hq=32, Hkv=8, MP=2, max_seq_len=32)
-    assert pa.pa_plan(short, cu_count=256)["num_splits"] == 1
+    ps = pa.pa_plan(short, cu_count=256)
+    assert ps["path"] == "decode" and ps["num_splits"] == 1
+    # few units with long contexts past the request limit -> equal split
+    d = desc(B=4100, Hq=4, Hkv=1, NP=600000, MP=128, max_seq_len=2048)
+    p = pa.pa_plan(d, cu_count=2048)
+    assert p["path"] == "decode_split" and p["num_splits"] > 1
+    assert p["workspace_bytes"] == pa.pa_workspace_bytes(d, p["num_splits"])
+    assert p["grid_x"] == 4100 * 1 * p["num_splits"]
 
 
 def test_workspace_bytes_formula():

@@ -224,6 +224,23 @@ def test_nan_poison_does_not_leak_and_padding_is_not_read():
     assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
 
 
+def test_bound_calls_match_the_wrappers():
+    b = ragged(49, [300, 1200, 2500, 40], 32, 8, 128)
+    dev = device_batch(b)
+    ref, ref_lse = run_decode(b, dev)
+    desc = pa.make_desc(dev["q"], dev["k_pool"], dev["page_table"], dev["seq_lens"], b.max_seq_len)
+    ws = torch.empty(max(pa.pa_plan(desc)["workspace_bytes"], 16), dtype=torch.uint8, device="cuda")
+    out, lse = torch.empty_like(ref), torch.empty_like(ref_lse)
+    call = pa.bind_decode(dev["q"], dev["k_pool"], dev["v_pool"], dev["page_table"],
+                          dev["seq_lens"], dev["q_offsets"], b.scale, out=out, lse=lse,
+                          workspace=ws, desc=desc)
+    for _ in range(3):
+        out.zero_()
+        call()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref) and torch.equal(lse, ref_lse)
+
+
 def test_empty_batch_is_a_no_op():
     b = ragged(47, [5], 8, 8, 128)
     dev = device_batch(b)
@@ -232,6 +249,91 @@ def test_empty_batch_is_a_no_op():
                             dev["seq_lens"][:0], dev["q_offsets"][:0], b.scale, max_seq_len=0)
     torch.cuda.synchronize()
     assert out.numel() == 0
+
+
+# ----------------------------------------------------------------------------
+# page-balanced decode: wave ranges that cross request boundaries
+# ----------------------------------------------------------------------------
+def guard_path(b, dev, max_seq_len=None):
+    desc = pa.make_desc(dev["q"], dev["k_pool"], dev["page_table"], dev["seq_lens"],
+                        max_seq_len or b.max_seq_len)
+    return pa.pa_plan(desc)
+
+
+def test_balanced_many_short_requests():
+    # ~1500 requests of 1..48 keys: every wave range spans several requests
+    rng = np.random.default_rng(60)
+    lens = rng.integers(1, 49, size=1500)
+    b = ragged(60, lens, 32, 8, 128)
+    dev = device_batch(b)
+    plan = guard_path(b, dev)
+    print(f"case balanced short requests plan={plan}", flush=True)
+    assert plan["path"] == "decode_balanced"
+    ro, rl = oracle_run(b)
+    out, lse = run_decode(b, dev)
+    compare(b, out, lse, ro, rl, label="balanced, 1500 short requests")
+
+
+def test_balanced_at_the_request_limit():
+    rng = np.random.default_rng(61)
+    lens = rng.integers(1, 33, size=4096)
+    b = ragged(61, lens, 8, 8, 64)
+    dev = device_batch(b)
+    plan = guard_path(b, dev)
+    print(f"case balanced 4096 requests plan={plan}", flush=True)
+    assert plan["path"] == "decode_balanced"
+    ro, rl = oracle_run(b)
+    out, lse = run_decode(b, dev)
+    compare(b, out, lse, ro, rl, label="balanced, 4096 requests")
+
+
+def test_balanced_fewer_pages_than_waves():
+    # the declared bound admits long contexts, the actual ones hold 11 pages:
+    # most waves own no page, a few own one
+    b = ragged(62, [37, 100, 5], 32, 8, 128)
+    dev = device_batch(b)
+    pad = torch.full((3, 200), -1, dtype=torch.int32, device="cuda")
+    dev["page_table"] = torch.cat([dev["page_table"], pad], dim=1).contiguous()
+    max_seq_len = dev["page_table"].shape[1] * 16
+    plan = guard_path(b, dev, max_seq_len)
+    print(f"case balanced sparse plan={plan}", flush=True)
+    assert plan["path"] == "decode_balanced"
+    ro, rl = oracle_run(b)
+    torch.cuda.synchronize()
+    out, lse = pa.pa_decode(dev["q"], dev["k_pool"], dev["v_pool"], dev["page_table"],
+                            dev["seq_lens"], dev["q_offsets"], b.scale, max_seq_len=max_seq_len)
+    torch.cuda.synchronize()
+    compare(b, out, lse, ro, rl, label="balanced, 11 pages")
+
+
+def test_balanced_one_long_request():
+    # every wave range lies inside the same request: V partials per head
+    b = ragged(63, [20000], 32, 8, 128)
+    dev = device_batch(b)
+    plan = guard_path(b, dev)
+    print(f"case balanced one request plan={plan}", flush=True)
+    assert plan["path"] == "decode_balanced"
+    ro, rl = oracle_run(b)
+    out, lse = run_decode(b, dev)
+    compare(b, out, lse, ro, rl, label="balanced, one 20000-key request")
+
+
+@pytest.mark.parametrize("Hq,Hkv,d,dtype", [(8, 8, 128, W.BF16), (16, 8, 128, W.BF16),
+                                            (32, 8, 64, W.BF16), (64, 8, 128, W.BF16),
+                                            (64, 8, 64, W.BF16), (64, 64, 128, W.BF16),
+                                            (16, 2, 128, W.BF16), (16, 4, 64, W.F32),
+                                            (8, 2, 128, W.F32)])
+def test_balanced_groups_dims_and_dtypes(Hq, Hkv, d, dtype):
+    rng = np.random.default_rng(64 + Hq + Hkv + d)
+    lens = np.concatenate([rng.integers(1, 3000, size=40), [16, 17, 1, 4096]])
+    b = ragged(64 + Hq + d, lens, Hq, Hkv, d, dtype=dtype)
+    dev = device_batch(b)
+    plan = guard_path(b, dev)
+    print(f"case balanced Hq={Hq} Hkv={Hkv} d={d} {dtype} plan={plan}", flush=True)
+    assert plan["path"] == "decode_balanced"
+    ro, rl = oracle_run(b)
+    out, lse = run_decode(b, dev)
+    compare(b, out, lse, ro, rl, label=f"balanced G={Hq // Hkv} Hkv={Hkv} d={d} {dtype}")
 
 
 # ----------------------------------------------------------------------------

@@ -142,3 +142,22 @@ def test_long_context_short_chunk_splits_across_workgroups():
                                      max_seq_len=b.max_seq_len, max_q_len=b.max_q_len)
     torch.cuda.synchronize()
     compare(b, out2, lse2, ro, rl, label="prefill unsplit")
+
+
+def test_bound_call_matches_the_wrapper():
+    b = chunk_batch(77, [600, 300, 129], [88, 0, 1], 32, 8, 128)
+    dev = device_batch(b)
+    ref, ref_lse = run_prefill(b, dev)
+    desc = pa.make_desc(dev["q"], dev["k_pool"], dev["page_table"], dev["seq_lens"], b.max_seq_len,
+                        b.max_q_len)
+    need = pa.pa_plan(desc)["workspace_bytes"]
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
+    out, lse = torch.empty_like(ref), torch.empty_like(ref_lse)
+    call = pa.bind_prefill_chunk(dev["q"], dev["k_pool"], dev["v_pool"], dev["page_table"],
+                                 dev["seq_lens"], dev["q_offsets"], b.scale, q_starts=None,
+                                 out=out, lse=lse, workspace=ws, desc=desc)
+    for _ in range(3):
+        out.zero_()
+        call()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref) and torch.equal(lse, ref_lse)
