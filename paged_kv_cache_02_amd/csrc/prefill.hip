@@ -8,16 +8,16 @@
 // matrix is stored.  The G query heads of a KV head are packed token-major:
 // packed row rho = token * G + h, so one K/V tile serves all of them (GQA).
 //
-// Work decomposition.  A workgroup of 2 waves owns a tile of 128 packed rows
-// of one (request, KV head) and, when the key range is long, one split of it:
-// the KV tiles of a long row tile are cut into splits of `kv_tiles_per_split`
-// tiles that run as separate workgroups and write partial results which a
-// merge pass combines by log-sum-exp, so long and short row tiles even out
-// across the CUs.
+// Work decomposition.  A workgroup of 8 waves owns a tile of 128 packed rows
+// of one (request, KV head): two wave groups of 4 waves each cover the same
+// 128 rows (32 per wave) and take the two halves of the tile's key range,
+// and at the end group 1 hands its state to group 0 through LDS, which
+// merges it lane by lane by the log-sum-exp rule.  When the grid holds fewer
+// workgroups than the chip has CUs, a long key range is further cut into
+// splits of `kv_tiles_per_split` KV tiles that run as separate workgroups
+// and write partial results, combined by a merge pass.
 //
-// Inside a workgroup, each wave owns 64 rows (two 32-row MFMA blocks that
-// share every operand read from LDS) and keys stream in tiles of 64 (4
-// pages):
+// Keys stream in tiles of 64 (4 pages); per wave group and KV tile:
 //   * K and V pages are copied straight from HBM into LDS with
 //     global_load_lds (no staging registers), double-buffered one tile
 //     ahead; 16-byte chunks of each key row are XOR-swizzled by key so the
@@ -246,7 +246,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a, int
   const int kt1 = min(kt0 + a.kv_tiles_per_split, tg.ntiles);
   const int q_start = q_start_of(a, r, lane);
 
-  // this lane's two query rows (row blocks rb = 0, 1)
+  // this lane's query row (one 32-row block per wave)
   const int Hq = a.num_q_heads;
   const int o = tg.o;
   int pos[kRB], tok[kRB], hh[kRB];
