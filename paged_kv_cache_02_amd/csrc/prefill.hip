@@ -56,6 +56,9 @@ constexpr int kLdsPages = 2048;                   // page ids kept in LDS
 constexpr float kRescaleLog2 = 8.0f;
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.4426950408889634f;
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedMfma = 0x0008;
+constexpr int kSchedDsRead = 0x0100;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short shortx4_t __attribute__((ext_vector_type(4)));
@@ -149,42 +152,41 @@ __device__ __forceinline__ int tile_page(const PageIds& pi, int kt, int m) {
   return __builtin_amdgcn_readfirstlane(id);
 }
 
-// DMA one KV tile (K and V) from the pool into an LDS stage.  Each of the 4
-// waves of a group moves a quarter of the 1 KB pieces; lane l of a piece fills LDS slot (key, chunk) =
-// (first key + l / kRowChunks, l % kRowChunks) with the key's chunk
-// (l % kRowChunks) ^ swz(key).  Pieces that hold keys at or past L, or lie on
-// a page past the needed ones, are written with ordinary loads of the live
-// keys and zeros for the rest (so a NaN in a page tail never reaches LDS).
+// DMA one KV tile (K and V) from the pool into an LDS stage.  The 1 KB
+// pieces of a tile split evenly over the 4 waves of a group so that wave w
+// moves exactly page w of the tile; `id` is that page's physical id
+// (uniform; -1 past the pages the request holds).  Lane l of a piece fills
+// LDS slot (key, chunk) = (first key + l / kRowChunks, l % kRowChunks) with
+// the key's chunk (l % kRowChunks) ^ swz(key).  A page whose keys are all
+// below L goes by DMA; a page holding keys at or past L (or no page) is
+// written with ordinary loads of the live keys and zeros for the rest, so a
+// NaN in a page tail never reaches LDS.
 template <int D>
 __device__ __forceinline__ void dma_tile(unsigned char* kst, unsigned char* vst,
                                          const __bf16* __restrict__ kpool,
-                                         const __bf16* __restrict__ vpool, const PageIds& pi,
-                                         int kt, int L, int Hkv, int g, int wave, int lane) {
+                                         const __bf16* __restrict__ vpool, int id, int kt, int L,
+                                         int Hkv, int g, int wave, int lane) {
   using GE = Geo<D>;
-  const size_t blk = (size_t)kPageSize * D;
-  const int kb = kt * kTileKeys;
   constexpr int kPerWave = GE::kDmaPerTile / kWavesPerGroup;
+  static_assert(kPerWave * GE::kKeysPerDma == kPageSize, "each wave moves one page");
+  const int key_base = kt * kTileKeys + wave * kPageSize;   // absolute key of the page's slot 0
+  const size_t page_off = ((size_t)(id < 0 ? 0 : id) * Hkv + g) * ((size_t)kPageSize * D);
+  const bool full = id >= 0 && key_base + kPageSize <= L;
 #pragma unroll
   for (int i = 0; i < kPerWave; ++i) {
-    const int u = wave * kPerWave + i;                   // 1 KB piece of the tile
-    const int key0 = u * GE::kKeysPerDma;                // first key of the piece (tile-relative)
-    const int pm = key0 / kPageSize;                     // page of the piece within the tile
-    const int id = tile_page(pi, kt, pm);
-    const int key = key0 + lane / GE::kRowChunks;        // this lane's key
+    const int u = wave * kPerWave + i;                     // 1 KB piece of the tile
+    const int slot = i * GE::kKeysPerDma + lane / GE::kRowChunks;   // key within the page
+    const int key = wave * kPageSize + slot;               // key within the tile
     const int chunk = (lane % GE::kRowChunks) ^ swz<D>(key);
-    const bool live = id >= 0 && kb + key < L;
-    const bool all_live = id >= 0 && kb + key0 + GE::kKeysPerDma <= L;
+    const size_t off = page_off + (size_t)slot * D + chunk * 8;
     unsigned char* kdst = kst + u * 1024;
     unsigned char* vdst = vst + u * 1024;
-    if (all_live) {
-      const size_t off = ((size_t)id * Hkv + g) * blk + (key % kPageSize) * D + chunk * 8;
+    if (full) {
       __builtin_amdgcn_global_load_lds(kpool + off, (lds_void*)kdst, 16, 0, 0);
       __builtin_amdgcn_global_load_lds(vpool + off, (lds_void*)vdst, 16, 0, 0);
     } else {
-      // partial piece: ordinary loads of the live keys, zeros elsewhere
       uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-      if (live) {
-        const size_t off = ((size_t)id * Hkv + g) * blk + (key % kPageSize) * D + chunk * 8;
+      if (id >= 0 && key_base + slot < L) {
         kv = *reinterpret_cast<const uint4*>(kpool + off);
         vv = *reinterpret_cast<const uint4*>(vpool + off);
       }
@@ -326,30 +328,47 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a, int
     // K operand address for k-step s: the swizzled chunk 2s + half of key
     // row kb2*32 + lrow sits at kbase ^ (32 s) (the swizzle is an XOR on
     // chunk bits 1..3, and the row base is a multiple of 256 bytes).
+    // All 8 K operands of a key block are requested before its MFMAs, and
+    // each register is refilled with the next block's operand as soon as its
+    // MFMA has been issued, so the MFMAs never wait on one LDS round trip
+    // each.
+    static_assert(kRB == 1, "the operand pipeline below is written for one row block");
     floatx16_t sacc[kRB][2];
+    uint32_t kbase[2];
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
       const int key = kb2 * 32 + lrow;
       const int sw = swz<D>(key);
-      uint32_t kbase = (uint32_t)(key * GE::kRowBytes) + ((uint32_t)(half ^ (sw & 1)) << 4) +
-                       ((uint32_t)(sw >> 1) << 5);
-      asm volatile("" : "+v"(kbase));   // keep the per-step addresses out of the loop preheader
-#pragma unroll
-      for (int s = 0; s < GE::kKSteps; ++s) {
-        const uint4 kv = *reinterpret_cast<const uint4*>(kst + (kbase ^ (uint32_t)(s << 5)));
-#pragma unroll
-        for (int rb = 0; rb < kRB; ++rb) {
-          if (s == 0) {
-            const floatx16_t zero = {};
-            sacc[rb][kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), as_bf16x8(qv[rb][0]),
-                                                                    zero, 0, 0, 0);
-          } else {
-            sacc[rb][kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), as_bf16x8(qv[rb][s]),
-                                                                    sacc[rb][kb2], 0, 0, 0);
-          }
-        }
-      }
+      kbase[kb2] = (uint32_t)(key * GE::kRowBytes) + ((uint32_t)(half ^ (sw & 1)) << 4) +
+                   ((uint32_t)(sw >> 1) << 5);
     }
+    asm volatile("" : "+v"(kbase[0]), "+v"(kbase[1]));   // keep the addresses out of the loop preheader
+    uint4 ka[GE::kKSteps];
+#pragma unroll
+    for (int s = 0; s < GE::kKSteps; ++s)
+      ka[s] = *reinterpret_cast<const uint4*>(kst + (kbase[0] ^ (uint32_t)(s << 5)));
+#pragma unroll
+    for (int s = 0; s < GE::kKSteps; ++s) {
+      const floatx16_t zero = {};
+      sacc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[s]), as_bf16x8(qv[0][s]),
+                                                           s == 0 ? zero : sacc[0][0], 0, 0, 0);
+      ka[s] = *reinterpret_cast<const uint4*>(kst + (kbase[1] ^ (uint32_t)(s << 5)));
+    }
+#pragma unroll
+    for (int s = 0; s < GE::kKSteps; ++s) {
+      const floatx16_t zero = {};
+      sacc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[s]), as_bf16x8(qv[0][s]),
+                                                           s == 0 ? zero : sacc[0][1], 0, 0, 0);
+    }
+    // schedule: the first block's reads, then each MFMA followed by the read
+    // that refills its operand register, then the second block's MFMAs
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, GE::kKSteps, 0);
+#pragma unroll
+    for (int s = 0; s < GE::kKSteps; ++s) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, GE::kKSteps, 0);
     // ---- mask, online softmax, P^T operand ----
     uint32_t pk[kRB][2][8];
 #pragma unroll
@@ -396,11 +415,11 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a, int
       }
       l_run[rb] += lsum;
     }
-    // ---- O^T += V^T P^T: 4 k-steps of 16 keys, 2 row blocks ----
+    // ---- O^T += V^T P^T: 4 k-steps of 16 keys ----
     // V operand: two transposing 8-byte reads per (k-step, dim block); with
-    // the XOR swizzle the address of dim block db is vbase ^ (64 db).
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    // the XOR swizzle the address of dim block db is vbase ^ (64 db).  The
+    // reads of k-step ks+1 are issued before the MFMAs of k-step ks.
+    auto v_operands = [&](int ks, uint4 (&av)[GE::kDimBlocks]) __attribute__((always_inline)) {
       const int kb2 = ks >> 1;
       const int th = ks & 1;
       // keys this lane addresses for the two transposing reads (e = 0..3, 4..7)
@@ -415,31 +434,47 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a, int
       uint32_t vbaseB = (uint32_t)(keyB * GE::kRowBytes) +
                         (((uint32_t)(c0 ^ (swB & 3)) << 4) | ((uint32_t)(swB & ~3) << 4)) + within;
       asm volatile("" : "+v"(vbaseA), "+v"(vbaseB));
-      uint4 pb[kRB];
-#pragma unroll
-      for (int rb = 0; rb < kRB; ++rb) {
-        pb[rb].x = pk[rb][kb2][4 * th + 0];
-        pb[rb].y = pk[rb][kb2][4 * th + 1];
-        pb[rb].z = pk[rb][kb2][4 * th + 2];
-        pb[rb].w = pk[rb][kb2][4 * th + 3];
-      }
 #pragma unroll
       for (int db = 0; db < GE::kDimBlocks; ++db) {
         const shortx4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) shortx4_t*)(vst + (vbaseA ^ (uint32_t)(db << 6))));
         const shortx4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) shortx4_t*)(vst + (vbaseB ^ (uint32_t)(db << 6))));
-        uint4 av;
-        av.x = __builtin_bit_cast(uint32_t, __builtin_shufflevector(va, va, 0, 1));
-        av.y = __builtin_bit_cast(uint32_t, __builtin_shufflevector(va, va, 2, 3));
-        av.z = __builtin_bit_cast(uint32_t, __builtin_shufflevector(vb, vb, 0, 1));
-        av.w = __builtin_bit_cast(uint32_t, __builtin_shufflevector(vb, vb, 2, 3));
+        av[db].x = __builtin_bit_cast(uint32_t, __builtin_shufflevector(va, va, 0, 1));
+        av[db].y = __builtin_bit_cast(uint32_t, __builtin_shufflevector(va, va, 2, 3));
+        av[db].z = __builtin_bit_cast(uint32_t, __builtin_shufflevector(vb, vb, 0, 1));
+        av[db].w = __builtin_bit_cast(uint32_t, __builtin_shufflevector(vb, vb, 2, 3));
+      }
+    };
+    uint4 avs[2][GE::kDimBlocks];
+    v_operands(0, avs[0]);
 #pragma unroll
-        for (int rb = 0; rb < kRB; ++rb)
-          oacc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(pb[rb]),
-                                                                 oacc[rb][db], 0, 0, 0);
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ks + 1 < 4) v_operands(ks + 1, avs[(ks + 1) & 1]);
+      const int kb2 = ks >> 1;
+      const int th = ks & 1;
+      uint4 pb;
+      pb.x = pk[0][kb2][4 * th + 0];
+      pb.y = pk[0][kb2][4 * th + 1];
+      pb.z = pk[0][kb2][4 * th + 2];
+      pb.w = pk[0][kb2][4 * th + 3];
+#pragma unroll
+      for (int db = 0; db < GE::kDimBlocks; ++db)
+        oacc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(avs[ks & 1][db]),
+                                                              as_bf16x8(pb), oacc[0][db], 0, 0, 0);
+    }
+    // schedule: k-step 0's reads, then each k-step's MFMAs interleaved with
+    // the next k-step's reads (two per MFMA), then the last MFMAs
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * GE::kDimBlocks, 1);
+#pragma unroll
+    for (int ks = 0; ks < 3; ++ks) {
+#pragma unroll
+      for (int db = 0; db < GE::kDimBlocks; ++db) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
       }
     }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, GE::kDimBlocks, 1);
   };
 
   // The two wave groups take the two halves of the key range, [kt0, mid)
@@ -458,18 +493,24 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a, int
     unsigned char* vs1 = GRP == 0 ? v_a1 : v_b1;
     const int my0 = GRP == 0 ? kt0 : mid;
     const int my1 = GRP == 0 ? mid : kt1;
-    if (my0 < my1) dma_tile<D>(ks0, vs0, kpool, vpool, pi, my0, L, Hkv, g, wave, lane);
+    // The page this wave moves for the next tile is looked up one step
+    // ahead (an LDS read whose latency the step's compute hides).
+    auto wave_page = [&](int kt) { return tile_page(pi, min(kt, my1 - 1), wave); };
+    if (my0 < my1) dma_tile<D>(ks0, vs0, kpool, vpool, wave_page(my0), my0, L, Hkv, g, wave, lane);
+    int next_id = wave_page(my0 + 1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int i = 0;;) {
       int kt = my0 + i;
-      if (kt + 1 < my1) dma_tile<D>(ks1, vs1, kpool, vpool, pi, kt + 1, L, Hkv, g, wave, lane);
+      if (kt + 1 < my1) dma_tile<D>(ks1, vs1, kpool, vpool, next_id, kt + 1, L, Hkv, g, wave, lane);
+      next_id = wave_page(kt + 2);
       if (kt < my1) compute_tile(ks0, vs0, kt * kTileKeys);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (++i >= nloop) break;
       kt = my0 + i;
-      if (kt + 1 < my1) dma_tile<D>(ks0, vs0, kpool, vpool, pi, kt + 1, L, Hkv, g, wave, lane);
+      if (kt + 1 < my1) dma_tile<D>(ks0, vs0, kpool, vpool, next_id, kt + 1, L, Hkv, g, wave, lane);
+      next_id = wave_page(kt + 2);
       if (kt < my1) compute_tile(ks1, vs1, kt * kTileKeys);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
