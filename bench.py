@@ -1,9 +1,10 @@
 """Benchmark: one mixed continuous-batching step of paged attention on one GPU.
 
 A step is one pass of the whole hot path over one batch that is resident in
-HBM: the dispatch guard plans each route, pa_prefill_chunk runs the prefill
-chunks (bf16 MFMA) and pa_decode runs the decode rows (split-K + log-sum-exp
-merge when the guard picks it).  The workload is the mixed step with
+HBM: pa_append_kv writes the step's new K/V rows into their page slots, the
+dispatch guard plans each route, pa_prefill_chunk runs the prefill chunks
+(bf16 MFMA) and pa_decode runs the decode rows (split-K + log-sum-exp merge
+when the guard picks it).  The workload is the mixed step with
 Qwen3-4B attention heads: 4 prefill chunks of 512 tokens at prior offsets
 0/512/1536/3072 plus 60 decode rows with contexts U[256, 4096]; 32 q heads,
 8 KV heads, d = 128, bf16, page size 16, permuted pool of 1.25x the pages.
@@ -99,6 +100,13 @@ def decode_alg_bytes(b) -> int:
     B, Hq, d = b.num_seqs, b.num_q_heads, b.head_dim
     return (keys * b.num_kv_heads * d * 2 * es + 2 * B * Hq * d * es + B * Hq * 4 + pages * 4
             + 2 * B * 4)
+
+
+def append_alg_bytes(b) -> int:
+    """The new K and V rows read once and written once into their slots, plus
+    the page-table entry each (row, KV head) write looks up."""
+    rows = int(b.total_q)
+    return 2 * 2 * rows * b.num_kv_heads * b.head_dim * 2 + rows * b.num_kv_heads * 4
 
 
 def prefill_alg_flops(b) -> int:
@@ -215,11 +223,28 @@ def main():
     pf_ws = (torch.empty(pf_plan["workspace_bytes"], dtype=torch.uint8, device=dev)
              if pf_plan["workspace_bytes"] else None)
 
-    # the two routes on each pool copy, with their arguments marshalled once
-    # so that the host stays ahead of the GPU and the kernels run back to back
+    # this step's new K/V rows (the prefill chunks' tokens and the decode
+    # tokens), written into their page slots before attention reads them
+    rng = np.random.default_rng(full.seed + 7)
+    def new_rows(b):
+        x = rng.standard_normal((b.total_q, b.num_kv_heads, b.head_dim)).astype(np.float32)
+        return to_dev(W.f32_to_bf16_bits(x), W.BF16)
+    ap = {"pf": (new_rows(pf), new_rows(pf)), "dc": (new_rows(dc), new_rows(dc))}
+    pf_ap_desc = pa.make_desc(ap["pf"][0], pools[0][0], pf_t["pt"], pf_t["sl"], pf.max_seq_len,
+                              pf.max_q_len)
+    dc_ap_desc = pa.make_desc(ap["dc"][0], pools[0][0], dc_t["pt"], dc_t["sl"], dc.max_seq_len, 1)
+
+    # the routes on each pool copy, with their arguments marshalled once so
+    # that the host stays ahead of the GPU and the kernels run back to back
     calls = {}
     for i in (0, 1):
         kp, vp = pools[i]
+        calls[("append_pf", i)] = pa.bind_append_kv(
+            ap["pf"][0], ap["pf"][1], kp, vp, pf_t["pt"], pf_t["sl"], pf_t["qo"],
+            q_starts=pf_t["qs"], desc=pf_ap_desc)
+        calls[("append_dc", i)] = pa.bind_append_kv(
+            ap["dc"][0], ap["dc"][1], kp, vp, dc_t["pt"], dc_t["sl"], dc_t["qo"], q_starts=None,
+            desc=dc_ap_desc)
         calls[("prefill", i)] = pa.bind_prefill_chunk(
             pf_t["q"], kp, vp, pf_t["pt"], pf_t["sl"], pf_t["qo"], pf.scale, q_starts=pf_t["qs"],
             out=pf_out, lse=pf_lse, workspace=pf_ws, desc=pf_desc)
@@ -228,6 +253,10 @@ def main():
             lse=dc_lse, workspace=ws, desc=dc_desc)
 
     def step(i, ev=None):
+        if ev is not None:
+            ev[3].record()
+        calls[("append_pf", i & 1)]()
+        calls[("append_dc", i & 1)]()
         if ev is not None:
             ev[0].record()
         calls[("prefill", i & 1)]()
@@ -243,7 +272,7 @@ def main():
 
     # timed region: exactly `steps` steps, events between the routes on the
     # stream the routes are launched on
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -253,6 +282,9 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     pf_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     dc_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    ap_ms = float(np.mean([e[3].elapsed_time(e[0]) for e in evs]))
+    ap_bytes = append_alg_bytes(pf) + append_alg_bytes(dc)
+    ap_gbs = ap_bytes / (ap_ms * 1e-3) / 1e9
 
     dec_bytes = decode_alg_bytes(dc)
     pf_flops = prefill_alg_flops(pf)
@@ -274,6 +306,10 @@ def main():
                               f"decode_kernel<bf16,128,4> x{dc_plan['num_splits']} + merge_kernel"),
                    "work": dec_bytes, "work_unit": "B"},
     }
+    kernels["append"] = {"bound": "hbm", "achieved": round(ap_gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(ap_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "ms": round(ap_ms, 4), "kernel": "append_kernel (prefill chunks + decode rows)",
+                         "work": ap_bytes, "work_unit": "B"}
     dominant = "prefill" if pf_ms >= dc_ms else "decode"
     roof = {k: kernels[dominant][k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
     roof["kernel"] = kernels[dominant]["kernel"]
@@ -293,6 +329,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "mixed continuous-batching step, Qwen3-4B attention heads (32q/8kv, d=128)",
+            "append": "new K/V rows of the step (2048 chunk tokens + 60 decode tokens) into their page slots",
             "prefill": "4 chunks x 512 tokens at offsets 0/512/1536/3072, causal",
             "decode": "60 rows, contexts U[256,4096], seed %d" % full.seed,
             "page_size": 16, "pool_pages": full.num_pages, "global_batch": 64,

@@ -26,7 +26,8 @@
  *    unimplemented shape (head_dim not 64/128, page_size not 16, fp32 prefill).
  *    PA_ERR_WORKSPACE: workspace smaller than the plan needs.  PA_ERR_HIP: a
  *    kernel launch failed.  PA_ERR_METADATA: pa_validate_metadata found a
- *    contract violation in the device arrays.
+ *    contract violation in the device arrays.  PA_ERR_NO_PAGES: the page pool
+ *    has fewer free pages than a request needs (nothing was allocated).
  *  - Layouts (row-major, contiguous):
  *      q, out      [total_q, Hq, d]       rows ordered by request, then token
  *      lse         float32 [total_q, Hq]  natural log of sum_j exp(scale*q.k_j)
@@ -66,7 +67,8 @@ typedef enum pa_status {
   PA_ERR_UNSUPPORTED = 2,
   PA_ERR_WORKSPACE = 3,
   PA_ERR_HIP = 4,
-  PA_ERR_METADATA = 5
+  PA_ERR_METADATA = 5,
+  PA_ERR_NO_PAGES = 6
 } pa_status;
 
 typedef enum pa_dtype { PA_BF16 = 0, PA_F32 = 1 } pa_dtype;
@@ -167,6 +169,48 @@ pa_status pa_prefill_chunk(const pa_desc* desc, const void* q, const void* k_poo
                            const int32_t* q_offsets, const int32_t* q_starts, float scale,
                            void* out, float* lse, void* workspace, size_t workspace_bytes,
                            void* stream);
+
+/* Append a step's new K and V rows into their page slots (the write that
+ * precedes attention in every serving step: the "Paged KV Cache" section of
+ * the tiny-llm source reading).  Request r contributes n_r = seq_lens[r] -
+ * q_offsets[r] rows (seq_lens after this append), packed like q: k_new,
+ * v_new [total_q, Hkv, d] of desc->dtype, rows by request then token.  Row i
+ * of request r (position p = q_offsets[r] + i) is copied bit-exactly to
+ * k_pool/v_pool[page_table[r][p / P], :, p % P, :].  q_starts: int32 [B+1]
+ * exclusive prefix sum of n_r, or NULL to derive it on the device.  The
+ * pages must already be in the table (pa_pool_reserve); rows whose page id
+ * lies outside [0, num_pages) are skipped, never written elsewhere.  Rows of
+ * different requests must map to different slots (requests own their pages).
+ * Works for bf16 and fp32, d = 64 or 128. */
+pa_status pa_append_kv(const pa_desc* desc, const void* k_new, const void* v_new,
+                       const int32_t* page_table, const int32_t* seq_lens,
+                       const int32_t* q_offsets, const int32_t* q_starts, void* k_pool,
+                       void* v_pool, void* stream);
+
+/* Host page allocator for the shared pool (pure host: no device memory, no
+ * synchronization).  Pages are handed out on demand and returned when a
+ * request finishes ("Paged KV Cache" in the tiny-llm source reading).  Every
+ * call is all-or-nothing and thread-safe.
+ *   pa_pool_create:  a pool of num_pages free pages, ids 0 .. num_pages-1.
+ *   pa_pool_alloc:   n free ids into ids[0..n); PA_ERR_NO_PAGES if fewer free.
+ *   pa_pool_free:    return n ids; PA_ERR_ARG (nothing freed) if an id is out
+ *                    of range, not allocated, or repeated.
+ *   pa_pool_reserve: grow one request's host page-table row from old_len to
+ *                    new_len keys: allocates the pages for logical pages
+ *                    ceil(old_len/P) .. ceil(new_len/P)-1 into the row
+ *                    (PA_ERR_ARG if that exceeds max_pages_per_seq).
+ *   pa_pool_release: return the ceil(len/P) pages of a row and set them to -1.
+ *   pa_pool_num_free: free pages, or -1 for a null pool. */
+typedef struct pa_page_pool pa_page_pool;
+pa_status pa_pool_create(int32_t num_pages, pa_page_pool** pool);
+void pa_pool_destroy(pa_page_pool* pool);
+int32_t pa_pool_num_free(pa_page_pool* pool);
+pa_status pa_pool_alloc(pa_page_pool* pool, int32_t n, int32_t* ids);
+pa_status pa_pool_free(pa_page_pool* pool, const int32_t* ids, int32_t n);
+pa_status pa_pool_reserve(pa_page_pool* pool, int32_t* page_table_row, int32_t max_pages_per_seq,
+                          int32_t old_len, int32_t new_len, int32_t page_size);
+pa_status pa_pool_release(pa_page_pool* pool, int32_t* page_table_row, int32_t max_pages_per_seq,
+                          int32_t len, int32_t page_size);
 
 /* Log-sum-exp merge of split partials (the merge pass on its own; a test
  * hook).  o_part float32 [rows, heads, S, d], lse_part float32 [rows, heads, S]

@@ -18,7 +18,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpa.so")
 
-PA_OK, PA_ERR_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_METADATA = range(6)
+PA_OK, PA_ERR_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_METADATA, PA_ERR_NO_PAGES = range(7)
 PA_BF16, PA_F32 = 0, 1
 PA_PATH_DECODE, PA_PATH_DECODE_SPLIT, PA_PATH_PREFILL, PA_PATH_DECODE_BALANCED = 0, 1, 2, 3
 PATH_NAMES = {PA_PATH_DECODE: "decode", PA_PATH_DECODE_SPLIT: "decode_split",
@@ -61,6 +61,15 @@ _SIGS = {
                                          ctypes.c_int32, _P, _P, _P, ctypes.c_int32, _P, _P]),
     "pa_gather_kv": (ctypes.c_int, [_D, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]),
     "pa_validate_metadata": (ctypes.c_int, [_D, _P, _P, _P, _P]),
+    "pa_append_kv": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "pa_pool_create": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p)]),
+    "pa_pool_destroy": (None, [_P]),
+    "pa_pool_num_free": (ctypes.c_int32, [_P]),
+    "pa_pool_alloc": (ctypes.c_int, [_P, ctypes.c_int32, _P]),
+    "pa_pool_free": (ctypes.c_int, [_P, _P, ctypes.c_int32]),
+    "pa_pool_reserve": (ctypes.c_int, [_P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_int32]),
+    "pa_pool_release": (ctypes.c_int, [_P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -294,7 +303,83 @@ def pa_validate_metadata(desc: pa_desc, page_table, seq_lens, q_offsets=None) ->
                                           _ptr(q_offsets), _stream(page_table.device)))
 
 
+def pa_append_kv(k_new, v_new, k_pool, v_pool, page_table, seq_lens, q_offsets, *,
+                 q_starts=None, max_seq_len=None, max_q_len=None, desc=None):
+    """Write the new K/V rows [total_q, Hkv, d] into their page slots (in
+    place in k_pool / v_pool)."""
+    desc = desc or make_desc(k_new, k_pool, page_table, seq_lens, max_seq_len, max_q_len, q_offsets)
+    _check(lib().pa_append_kv(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(page_table),
+                              _ptr(seq_lens), _ptr(q_offsets), _ptr(q_starts), _ptr(k_pool),
+                              _ptr(v_pool), _stream(k_new.device)), "pa_append_kv")
+
+
+def bind_append_kv(k_new, v_new, k_pool, v_pool, page_table, seq_lens, q_offsets, *, q_starts,
+                   desc) -> BoundCall:
+    """pa_append_kv with fixed arguments (see BoundCall)."""
+    keep = (desc, k_new, v_new, k_pool, v_pool, page_table, seq_lens, q_offsets, q_starts)
+    return BoundCall("pa_append_kv", keep, ctypes.byref(desc), _ptr(k_new), _ptr(v_new),
+                     _ptr(page_table), _ptr(seq_lens), _ptr(q_offsets), _ptr(q_starts),
+                     _ptr(k_pool), _ptr(v_pool), _stream(k_new.device))
+
+
+class PagePool:
+    """The library's host page allocator (pa_pool_*): page ids on demand, a
+    request's page-table row grown by whole pages and released at the end.
+    Page-table rows are host numpy int32 arrays; copy them to the device
+    before a kernel reads them."""
+
+    def __init__(self, num_pages: int):
+        h = ctypes.c_void_p()
+        _check(lib().pa_pool_create(int(num_pages), ctypes.byref(h)), "pa_pool_create")
+        self._h = h
+        self.num_pages = int(num_pages)
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().pa_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def num_free(self) -> int:
+        return int(lib().pa_pool_num_free(self._h))
+
+    @staticmethod
+    def _i32(a):
+        import numpy as np
+        if not (isinstance(a, np.ndarray) and a.dtype == np.int32 and a.flags.c_contiguous):
+            raise ValueError("page-table rows and id lists must be contiguous int32 numpy arrays")
+        return a.ctypes.data_as(ctypes.c_void_p)
+
+    def alloc(self, n: int):
+        import numpy as np
+        ids = np.empty(max(int(n), 0), np.int32)
+        _check(lib().pa_pool_alloc(self._h, int(n), self._i32(ids) if n > 0 else None), "pa_pool_alloc")
+        return ids
+
+    def free(self, ids):
+        import numpy as np
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        _check(lib().pa_pool_free(self._h, self._i32(ids) if ids.size else None, int(ids.size)),
+               "pa_pool_free")
+
+    def reserve(self, row, old_len: int, new_len: int, page_size: int = 16):
+        """Grow page-table row `row` (int32 numpy view, edited in place)."""
+        _check(lib().pa_pool_reserve(self._h, self._i32(row), int(row.size), int(old_len),
+                                     int(new_len), int(page_size)), "pa_pool_reserve")
+
+    def release(self, row, length: int, page_size: int = 16):
+        _check(lib().pa_pool_release(self._h, self._i32(row), int(row.size), int(length),
+                                     int(page_size)), "pa_pool_release")
+
+
 __all__ = ["pa_desc", "pa_plan_info", "PaError", "lib", "make_desc", "pa_plan",
            "pa_workspace_bytes", "pa_decode", "pa_split_merge", "pa_prefill_chunk",
            "pa_merge_partials", "pa_gather_kv", "pa_validate_metadata", "pa_status_str",
-           "split_partials_view", "EXPORTED"]
+           "split_partials_view", "pa_append_kv", "bind_append_kv", "PagePool", "BoundCall",
+           "bind_decode", "bind_prefill_chunk", "EXPORTED"]

@@ -258,6 +258,7 @@ const char* pa_status_str(pa_status s) {
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace too small";
     case PA_ERR_HIP: return "PA_ERR_HIP: kernel launch failed";
     case PA_ERR_METADATA: return "PA_ERR_METADATA: device metadata violates the contract";
+    case PA_ERR_NO_PAGES: return "PA_ERR_NO_PAGES: the page pool has too few free pages";
   }
   return "unknown pa_status";
 }
@@ -410,6 +411,41 @@ pa_status pa_prefill_chunk(const pa_desc* d, const void* q, const void* k_pool,
   const hipError_t e = pa::launch_prefill(a, d->head_dim, G, reinterpret_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported) return PA_ERR_UNSUPPORTED;
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_append_kv(const pa_desc* d, const void* k_new, const void* v_new,
+                       const int32_t* page_table, const int32_t* seq_lens,
+                       const int32_t* q_offsets, const int32_t* q_starts, void* k_pool,
+                       void* v_pool, void* stream) {
+  pa_status st = check_desc(d);
+  if (st != PA_OK) return st;
+  if (d->num_seqs == 0 || d->total_q == 0) return PA_OK;
+  if (!k_new || !v_new || !page_table || !seq_lens || !q_offsets || !k_pool || !v_pool)
+    return PA_ERR_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool) ||
+      !aligned4(page_table) || !aligned4(seq_lens) || !aligned4(q_offsets) ||
+      (q_starts && !aligned4(q_starts)))
+    return PA_ERR_ARG;
+  if (d->max_q_len < 1) return PA_ERR_ARG;
+  pa::AppendArgs a;
+  memset(&a, 0, sizeof(a));
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.page_table = page_table;
+  a.seq_lens = seq_lens;
+  a.q_offsets = q_offsets;
+  a.q_starts = q_starts;
+  a.num_seqs = d->num_seqs;
+  a.num_kv_heads = d->num_kv_heads;
+  a.max_pages_per_seq = d->max_pages_per_seq;
+  a.num_pages = d->num_pages;
+  a.head_bytes = d->head_dim * elem_bytes(d->dtype);
+  const int rpw = pa::append_rows_per_wg();
+  a.tiles_per_seq = (d->max_q_len + rpw - 1) / rpw;
+  return pa::launch_append(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK
+                                                                                    : PA_ERR_HIP;
 }
 
 pa_status pa_merge_partials(int32_t rows, int32_t heads, int32_t num_splits, int32_t head_dim,

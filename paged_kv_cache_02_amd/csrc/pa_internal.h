@@ -90,6 +90,26 @@ int prefill_tile_keys();
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int group, hipStream_t s);
 
 // ---------------------------------------------------------------------------
+// KV append (new rows into their page slots)
+// ---------------------------------------------------------------------------
+struct AppendArgs {
+  const void* k_new;        // [total_q, Hkv, d] rows by request then token
+  const void* v_new;
+  void* k_pool;             // [NP, Hkv, P, d]
+  void* v_pool;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  const int32_t* q_offsets;
+  const int32_t* q_starts;  // [B+1] or null (derived on the device)
+  int32_t num_seqs, num_kv_heads, max_pages_per_seq, num_pages;
+  int32_t head_bytes;       // d * element size (a multiple of 16)
+  int32_t tiles_per_seq;    // row groups per request in the grid
+};
+
+int append_rows_per_wg();
+hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------------------
 // page gather (test hook)
 // ---------------------------------------------------------------------------
 struct GatherArgs {

@@ -33,7 +33,7 @@ def desc(B=32, Hq=16, Hkv=8, d=128, P=16, NP=4096, MP=128, total_q=None, max_seq
 
 
 def test_status_strings():
-    for code in range(6):
+    for code in range(7):
         assert pa.pa_status_str(code).startswith("PA_")
 
 
