@@ -60,6 +60,9 @@ __global__ void __launch_bounds__(kThreads) append_kernel(AppendArgs a) {
   unsigned char* __restrict__ vp = reinterpret_cast<unsigned char*>(a.v_pool);
   const size_t block_bytes = (size_t)kPageSize * a.head_bytes;   // one (page, KV head) block
 
+  // unrolled so that several independent page-id -> load -> store chains
+  // are in flight per thread
+#pragma unroll 4
   for (int x = threadIdx.x; x < rows * row_chunks; x += kThreads) {
     const int i = x / row_chunks;            // row within the group
     const int w = x % row_chunks;
