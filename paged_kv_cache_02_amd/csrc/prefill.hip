@@ -20,13 +20,16 @@
 // Keys stream in tiles of 64 (4 pages); per wave group and KV tile:
 //   * K and V pages are copied straight from HBM into LDS with
 //     global_load_lds (no staging registers), double-buffered one tile
-//     ahead; 16-byte chunks of each key row are XOR-swizzled by key so the
-//     operand reads below are bank-conflict free;
+//     ahead; K's 16-byte chunks are XOR-swizzled by key and V is stored as
+//     [dim block][key] within each 1 KB piece, so the operand reads below
+//     are bank-conflict free and every V read is one register plus an
+//     immediate offset;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: A = K rows read from LDS,
 //     B = Q held in registers, so a lane owns one query row and 16 of every
 //     32 keys -- the row max and sum need one exchange with lane ^ 32;
 //   * causal mask by select on diagonal tiles only; lazy online-softmax
-//     rescale (only when the max grows by more than 2^8);
+//     rescale (only when the max grows by more than 2^8); the row max and
+//     sum cross the two lane halves with permlane32_swap;
 //   * P is rounded to bf16 and O^T += V^T P^T: the V^T operand comes from
 //     V's natural [key][dim] layout through ds_read_b64_tr_b16 (gfx950's
 //     transposing LDS read), in the key order the P^T registers carry, and
@@ -74,13 +77,16 @@ struct Geo {
   static constexpr int kDmaPerTile = kTileBytes / 1024;  // per K (and per V) tile
   static constexpr int kKSteps = D / 16;              // MFMA k-steps over the head dim
   static constexpr int kDimBlocks = D / 32;           // 32-dim output blocks
+  // byte offsets in a V stage ([1 KB piece of kKeysPerDma keys][dim block][key][4 chunks])
+  static constexpr int kVDimBlockBytes = kKeysPerDma * 64;
+  static constexpr int kVKeys8Bytes = (8 / kKeysPerDma) * 1024;   // 8 keys further on
+  static constexpr int kVKStepBytes = (16 / kKeysPerDma) * 1024;  // 16 keys further on
 };
 
-// XOR swizzle of 16-byte chunk indices within a key row.  For d = 128 (16
+// XOR swizzle of 16-byte chunk indices within a K row.  For d = 128 (16
 // chunks per 256-byte row, LDS serving 256 bytes per cycle) it is a bijection
 // on 16 consecutive keys, so the 16 rows of one K operand read land on 16
-// different chunks, and its bits 2..3 follow key & 3, so the 4 consecutive
-// keys of one transposing V read land in 4 different 64-byte bank quads.
+// different chunks.
 template <int D>
 __device__ __forceinline__ int swz(int key) {
   return D == 128 ? (((key & 3) << 2) | ((key >> 2) & 3)) : ((key >> 1) & 3);
@@ -97,6 +103,35 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+// Max and sum of x over lanes l and l ^ 32, without an LDS round trip:
+// permlane32_swap with both operands x returns x of this lane in one result
+// and x of lane ^ 32 in the other, so combining the two results with a
+// symmetric operation needs no knowledge of which is which.  The second
+// operand passes through an empty asm statement: given the same value
+// twice, the compiler would otherwise take the two results as equal and
+// drop one of them.
+__device__ __forceinline__ void lane_pair(float x, float& a, float& b) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  uint32_t w = u;
+  asm volatile("" : "+v"(w));
+  const auto pr = __builtin_amdgcn_permlane32_swap(u, w, false, false);
+  const uint32_t r0 = pr[0], r1 = pr[1];   // copied out: a bit cast of a vector element reads element 0
+  a = __builtin_bit_cast(float, r0);
+  b = __builtin_bit_cast(float, r1);
+}
+
+__device__ __forceinline__ float pair_max(float x) {
+  float a, b;
+  lane_pair(x, a, b);
+  return fmaxf(a, b);
+}
+
+__device__ __forceinline__ float pair_sum(float x) {
+  float a, b;
+  lane_pair(x, a, b);
+  return a + b;
+}
 
 // Geometry of one (request, row tile) shared by the attention kernel and the
 // merge pass.
@@ -175,21 +210,24 @@ __device__ __forceinline__ void dma_tile(unsigned char* kst, unsigned char* vst,
 #pragma unroll
   for (int i = 0; i < kPerWave; ++i) {
     const int u = wave * kPerWave + i;                     // 1 KB piece of the tile
-    const int slot = i * GE::kKeysPerDma + lane / GE::kRowChunks;   // key within the page
-    const int key = wave * kPageSize + slot;               // key within the tile
-    const int chunk = (lane % GE::kRowChunks) ^ swz<D>(key);
-    const size_t off = page_off + (size_t)slot * D + chunk * 8;
+    // K: key rows in order, 16-byte chunks XOR-swizzled by key
+    const int kslot = i * GE::kKeysPerDma + lane / GE::kRowChunks;   // key within the page
+    const int kchunk = (lane % GE::kRowChunks) ^ swz<D>(wave * kPageSize + kslot);
+    const size_t koff = page_off + (size_t)kslot * D + kchunk * 8;
+    // V: the piece's keys as [dim block][key][4 chunks], so the transposing
+    // reads of one dim block touch kKeysPerDma x 64 consecutive bytes
+    const int vslot = i * GE::kKeysPerDma + (lane / 4) % GE::kKeysPerDma;
+    const int vchunk = 4 * (lane / (4 * GE::kKeysPerDma)) + (lane & 3);
+    const size_t voff = page_off + (size_t)vslot * D + vchunk * 8;
     unsigned char* kdst = kst + u * 1024;
     unsigned char* vdst = vst + u * 1024;
     if (full) {
-      __builtin_amdgcn_global_load_lds(kpool + off, (lds_void*)kdst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vpool + off, (lds_void*)vdst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(kpool + koff, (lds_void*)kdst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vpool + voff, (lds_void*)vdst, 16, 0, 0);
     } else {
       uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-      if (id >= 0 && key_base + slot < L) {
-        kv = *reinterpret_cast<const uint4*>(kpool + off);
-        vv = *reinterpret_cast<const uint4*>(vpool + off);
-      }
+      if (id >= 0 && key_base + kslot < L) kv = *reinterpret_cast<const uint4*>(kpool + koff);
+      if (id >= 0 && key_base + vslot < L) vv = *reinterpret_cast<const uint4*>(vpool + voff);
       *reinterpret_cast<uint4*>(kdst + lane * 16) = kv;
       *reinterpret_cast<uint4*>(vdst + lane * 16) = vv;
     }
@@ -206,15 +244,18 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a, int
   using GE = Geo<D>;
   static_assert(kRB == 1, "the wave-group merge is written for one row block per wave");
   // two LDS stages per wave group, each K + V, named statically so the
-  // compiler can tell the tile being copied in from the tile being read
+  // compiler can tell the tile being copied in from the tile being read.
+  // The V stages are laid out first (LDS variables are placed by decreasing
+  // alignment), so every V operand address is one register plus an
+  // immediate offset below 64 KB.
+  __shared__ __align__(2048) unsigned char v_a0[GE::kTileBytes];
+  __shared__ __align__(2048) unsigned char v_a1[GE::kTileBytes];
+  __shared__ __align__(2048) unsigned char v_b0[GE::kTileBytes];
+  __shared__ __align__(2048) unsigned char v_b1[GE::kTileBytes];
   __shared__ __align__(1024) unsigned char k_a0[GE::kTileBytes];
-  __shared__ __align__(1024) unsigned char v_a0[GE::kTileBytes];
   __shared__ __align__(1024) unsigned char k_a1[GE::kTileBytes];
-  __shared__ __align__(1024) unsigned char v_a1[GE::kTileBytes];
   __shared__ __align__(1024) unsigned char k_b0[GE::kTileBytes];
-  __shared__ __align__(1024) unsigned char v_b0[GE::kTileBytes];
   __shared__ __align__(1024) unsigned char k_b1[GE::kTileBytes];
-  __shared__ __align__(1024) unsigned char v_b1[GE::kTileBytes];
   __shared__ int s_pages[kLdsPages];
   __shared__ float s_ml[kWavesPerGroup][2][64];
 
@@ -314,11 +355,16 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a, int
   const float sl2 = a.scale_log2;
 
   // lanes of a 16-lane group address 4 keys x 4 dim quads for the
-  // transposing reads of the V^T operand
+  // transposing reads of the V^T operand: key 4 * half + vk (plus 16 per
+  // k-step and 8 for the second read), dims vdim_off .. vdim_off + 3 of a
+  // 32-dim block; vlane is that element's byte offset in a V stage
   const int vgrp = lane >> 4;
   const int vp = lane & 15;
   const int vk = vp >> 2;                                 // which of the 4 keys
   const int vdim_off = 16 * (vgrp & 1) + 4 * (vp & 3);   // dims within a 32-dim block
+  const int vkey = 4 * half + vk;
+  const uint32_t vlane = (uint32_t)((vkey / GE::kKeysPerDma) * 1024 + (vkey % GE::kKeysPerDma) * 64 +
+                                    (vdim_off >> 3) * 16 + (vdim_off & 7) * 2);
 
   // one KV tile out of an LDS stage
   auto compute_tile = [&](const unsigned char* kst, const unsigned char* vst, int kb)
@@ -374,20 +420,20 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a, int
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
       if (kb + kTileKeys - 1 > pos_lo) {
+        // element i of key block kb2 holds key kb + kb2*32 + 8*(i/4) + 4*half + i%4
+        const int lim = pos[rb] - kb - 4 * half;
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kb + kb2 * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-            sacc[rb][kb2][i] = key <= pos[rb] ? sacc[rb][kb2][i] : -INFINITY;
-          }
+          for (int i = 0; i < 16; ++i)
+            sacc[rb][kb2][i] = kb2 * 32 + 8 * (i / 4) + (i % 4) <= lim ? sacc[rb][kb2][i] : -INFINITY;
       }
       float tmax = -INFINITY;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
         for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[rb][kb2][i]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * sl2;   // scale > 0 commutes with max
+      tmax = pair_max(tmax) * sl2;   // scale > 0 commutes with max
       const bool need = tmax > m_run[rb] + kRescaleLog2;
       if (__builtin_expect(__any(need), 0)) {
         const float mn = fmaxf(m_run[rb], tmax);
@@ -402,6 +448,9 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a, int
       // a row with no visible key so far keeps m = -inf: use 0 as the
       // reference so its (all -inf) scores give p = 0 rather than NaN
       const float mref = m_run[rb] == -INFINITY ? 0.f : m_run[rb];
+      // the row sum adds the fp32 weights (a sum of their bf16 roundings
+      // would be off by up to 2^-9 relative in a row with one dominant key,
+      // about 2e-3 in the log-sum-exp)
       float lsum = 0.f;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
@@ -416,30 +465,17 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a, int
       l_run[rb] += lsum;
     }
     // ---- O^T += V^T P^T: 4 k-steps of 16 keys ----
-    // V operand: two transposing 8-byte reads per (k-step, dim block); with
-    // the XOR swizzle the address of dim block db is vbase ^ (64 db).  The
-    // reads of k-step ks+1 are issued before the MFMAs of k-step ks.
+    // V operand: two transposing 8-byte reads per (k-step, dim block), all
+    // at fixed offsets from one per-lane address.  The reads of k-step ks+1
+    // are issued before the MFMAs of k-step ks.
     auto v_operands = [&](int ks, uint4 (&av)[GE::kDimBlocks]) __attribute__((always_inline)) {
-      const int kb2 = ks >> 1;
-      const int th = ks & 1;
-      // keys this lane addresses for the two transposing reads (e = 0..3, 4..7)
-      const int keyA = kb2 * 32 + 16 * th + 4 * half + vk;
-      const int keyB = keyA + 8;
-      const int c0 = vdim_off >> 3;                 // chunk of dims within a 32-dim block
-      const int within = (vdim_off & 7) * 2;        // byte offset inside the chunk
-      const int swA = swz<D>(keyA);
-      const int swB = swz<D>(keyB);
-      uint32_t vbaseA = (uint32_t)(keyA * GE::kRowBytes) +
-                        (((uint32_t)(c0 ^ (swA & 3)) << 4) | ((uint32_t)(swA & ~3) << 4)) + within;
-      uint32_t vbaseB = (uint32_t)(keyB * GE::kRowBytes) +
-                        (((uint32_t)(c0 ^ (swB & 3)) << 4) | ((uint32_t)(swB & ~3) << 4)) + within;
-      asm volatile("" : "+v"(vbaseA), "+v"(vbaseB));
 #pragma unroll
       for (int db = 0; db < GE::kDimBlocks; ++db) {
+        const unsigned char* pa = vst + vlane + ks * GE::kVKStepBytes + db * GE::kVDimBlockBytes;
         const shortx4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) shortx4_t*)(vst + (vbaseA ^ (uint32_t)(db << 6))));
+            (__attribute__((address_space(3))) shortx4_t*)(pa));
         const shortx4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) shortx4_t*)(vst + (vbaseB ^ (uint32_t)(db << 6))));
+            (__attribute__((address_space(3))) shortx4_t*)(pa + GE::kVKeys8Bytes));
         av[db].x = __builtin_bit_cast(uint32_t, __builtin_shufflevector(va, va, 0, 1));
         av[db].y = __builtin_bit_cast(uint32_t, __builtin_shufflevector(va, va, 2, 3));
         av[db].z = __builtin_bit_cast(uint32_t, __builtin_shufflevector(vb, vb, 0, 1));
@@ -570,7 +606,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a, int
   const size_t unit = ((size_t)r * T + t) * Hkv + g;
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
-    const float l_tot = l_run[rb] + __shfl_xor(l_run[rb], 32);
+    const float l_tot = pair_sum(l_run[rb]);
     if (!row_valid[rb]) continue;
     const bool empty = !(l_tot > 0.f);
     const float inv = empty ? 0.f : 1.f / l_tot;
