@@ -189,28 +189,61 @@ pa_status pa_append_kv(const pa_desc* desc, const void* k_new, const void* v_new
 
 /* Host page allocator for the shared pool (pure host: no device memory, no
  * synchronization).  Pages are handed out on demand and returned when a
- * request finishes ("Paged KV Cache" in the tiny-llm source reading).  Every
- * call is all-or-nothing and thread-safe.
- *   pa_pool_create:  a pool of num_pages free pages, ids 0 .. num_pages-1.
- *   pa_pool_alloc:   n free ids into ids[0..n); PA_ERR_NO_PAGES if fewer free.
- *   pa_pool_free:    return n ids; PA_ERR_ARG (nothing freed) if an id is out
- *                    of range, not allocated, or repeated.
- *   pa_pool_reserve: grow one request's host page-table row from old_len to
- *                    new_len keys: allocates the pages for logical pages
- *                    ceil(old_len/P) .. ceil(new_len/P)-1 into the row
- *                    (PA_ERR_ARG if that exceeds max_pages_per_seq).
- *   pa_pool_release: return the ceil(len/P) pages of a row and set them to -1.
+ * request finishes ("Paged KV Cache" in the tiny-llm source reading).  A page
+ * may be held by several page tables at once (a shared prompt prefix, the
+ * reference-count reuse of "mini-vllm-tutorial advanced-series design",
+ * Phase C, adv05): it keeps one reference per holder and returns to the free
+ * list when the last one is dropped.  Every call is all-or-nothing and
+ * thread-safe.
+ *   pa_pool_create:   a pool of num_pages free pages, ids 0 .. num_pages-1.
+ *   pa_pool_alloc:    n free ids into ids[0..n), one reference each;
+ *                     PA_ERR_NO_PAGES if fewer are free.
+ *   pa_pool_free:     drop one reference per listed id; PA_ERR_ARG (nothing
+ *                     changes) if an id is out of range or listed more often
+ *                     than it is held.
+ *   pa_pool_share:    add one reference per listed id (each must be held).
+ *   pa_pool_refcount: references held on page id; -1 if out of range.
+ *   pa_pool_reserve:  grow one request's host page-table row from old_len to
+ *                     new_len keys: allocates the pages for logical pages
+ *                     ceil(old_len/P) .. ceil(new_len/P)-1 into the row
+ *                     (PA_ERR_ARG if that exceeds max_pages_per_seq).
+ *   pa_pool_release:  drop the row's references on its ceil(len/P) pages and
+ *                     set those entries to -1.
+ *   pa_pool_fork:     start dst_row as a sharer of src_row's first
+ *                     ceil(len/P) pages (a new request with the same prefix):
+ *                     copies the ids and adds one reference each.
+ *   pa_pool_cow:      before writing into logical page lp of a row: if the
+ *                     row is the page's only holder, *old_id = *new_id = the
+ *                     page and nothing changes; otherwise a free page
+ *                     replaces it in the row (one reference moves over) and
+ *                     *old_id, *new_id name the pair whose contents the caller
+ *                     copies with pa_copy_pages before writing.
+ *                     PA_ERR_NO_PAGES if no page is free.
  *   pa_pool_num_free: free pages, or -1 for a null pool. */
 typedef struct pa_page_pool pa_page_pool;
 pa_status pa_pool_create(int32_t num_pages, pa_page_pool** pool);
 void pa_pool_destroy(pa_page_pool* pool);
 int32_t pa_pool_num_free(pa_page_pool* pool);
+int32_t pa_pool_refcount(pa_page_pool* pool, int32_t id);
 pa_status pa_pool_alloc(pa_page_pool* pool, int32_t n, int32_t* ids);
 pa_status pa_pool_free(pa_page_pool* pool, const int32_t* ids, int32_t n);
+pa_status pa_pool_share(pa_page_pool* pool, const int32_t* ids, int32_t n);
 pa_status pa_pool_reserve(pa_page_pool* pool, int32_t* page_table_row, int32_t max_pages_per_seq,
                           int32_t old_len, int32_t new_len, int32_t page_size);
 pa_status pa_pool_release(pa_page_pool* pool, int32_t* page_table_row, int32_t max_pages_per_seq,
                           int32_t len, int32_t page_size);
+pa_status pa_pool_fork(pa_page_pool* pool, const int32_t* src_row, int32_t* dst_row,
+                       int32_t max_pages_per_seq, int32_t len, int32_t page_size);
+pa_status pa_pool_cow(pa_page_pool* pool, int32_t* page_table_row, int32_t max_pages_per_seq,
+                      int32_t logical_page, int32_t* old_id, int32_t* new_id);
+
+/* Copy whole pages, K and V for every KV head, from src_ids[i] to
+ * dst_ids[i] (device int32 arrays of n ids; bit-exact): the device half of
+ * pa_pool_cow.  A pair naming a page outside [0, num_pages), or the same
+ * page twice, is skipped.  The dst pages must be distinct and none of them a
+ * src page of the same call. */
+pa_status pa_copy_pages(const pa_desc* desc, void* k_pool, void* v_pool, const int32_t* src_ids,
+                        const int32_t* dst_ids, int32_t n, void* stream);
 
 /* Log-sum-exp merge of split partials (the merge pass on its own; a test
  * hook).  o_part float32 [rows, heads, S, d], lse_part float32 [rows, heads, S]

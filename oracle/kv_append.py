@@ -23,6 +23,13 @@ Parity pins (tests/test_oracle_append.py): gathering the appended positions
 back through the independently pinned `gather` returns the new rows exactly;
 with an identity page table the pool equals a dense [B, T, Hkv, d] cache
 written by slicing; every slot that no new row maps to is left unchanged.
+
+`copy_pages` is the device half of a copy on write for shared prefix pages
+("mini-vllm-tutorial advanced-series design", Phase C, adv05: pages shared
+by several requests are copied before one of them writes): page dst[i]
+becomes a copy of page src[i], K and V, every KV head.  Pins: a table that
+names dst gathers what the same table naming src gathered; every other page
+is unchanged.
 """
 from __future__ import annotations
 
@@ -52,4 +59,20 @@ def append_kv(k_pool: np.ndarray, v_pool: np.ndarray, page_table: np.ndarray,
             v_out[page, :, slot, :] = v_new[row]
             row += 1
     assert row == k_new.shape[0], "k_new rows must equal sum of seq_lens - q_offsets"
+    return k_out, v_out
+
+
+def copy_pages(k_pool: np.ndarray, v_pool: np.ndarray, src, dst) -> Tuple[np.ndarray, np.ndarray]:
+    """Return copies of the pools with page dst[i] replaced by page src[i]
+    (K and V, all KV heads).  Pairs naming a page outside the pool, or the
+    same page twice, are skipped."""
+    k_out = k_pool.copy()
+    v_out = v_pool.copy()
+    num_pages = k_pool.shape[0]
+    for s_id, d_id in zip(src, dst):
+        s_id, d_id = int(s_id), int(d_id)
+        if not (0 <= s_id < num_pages and 0 <= d_id < num_pages) or s_id == d_id:
+            continue
+        k_out[d_id] = k_pool[s_id]
+        v_out[d_id] = v_pool[s_id]
     return k_out, v_out

@@ -70,6 +70,11 @@ _SIGS = {
     "pa_pool_reserve": (ctypes.c_int, [_P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                        ctypes.c_int32]),
     "pa_pool_release": (ctypes.c_int, [_P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]),
+    "pa_pool_refcount": (ctypes.c_int32, [_P, ctypes.c_int32]),
+    "pa_pool_share": (ctypes.c_int, [_P, _P, ctypes.c_int32]),
+    "pa_pool_fork": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]),
+    "pa_pool_cow": (ctypes.c_int, [_P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P]),
+    "pa_copy_pages": (ctypes.c_int, [_D, _P, _P, _P, _P, ctypes.c_int32, _P]),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -322,9 +327,21 @@ def bind_append_kv(k_new, v_new, k_pool, v_pool, page_table, seq_lens, q_offsets
                      _ptr(k_pool), _ptr(v_pool), _stream(k_new.device))
 
 
+def pa_copy_pages(k_pool, v_pool, src_ids, dst_ids, *, desc):
+    """Copy whole pages (K and V, all KV heads) src_ids[i] -> dst_ids[i]
+    (device int32 tensors), in place in the pools: the device half of a
+    copy on write (PagePool.cow)."""
+    n = int(src_ids.numel())
+    if int(dst_ids.numel()) != n:
+        raise ValueError("src_ids and dst_ids must have the same length")
+    _check(lib().pa_copy_pages(ctypes.byref(desc), _ptr(k_pool), _ptr(v_pool), _ptr(src_ids),
+                               _ptr(dst_ids), n, _stream(k_pool.device)), "pa_copy_pages")
+
+
 class PagePool:
     """The library's host page allocator (pa_pool_*): page ids on demand, a
-    request's page-table row grown by whole pages and released at the end.
+    request's page-table row grown by whole pages and released at the end,
+    pages shared between rows by reference count with copy on write.
     Page-table rows are host numpy int32 arrays; copy them to the device
     before a kernel reads them."""
 
@@ -377,9 +394,32 @@ class PagePool:
         _check(lib().pa_pool_release(self._h, self._i32(row), int(row.size), int(length),
                                      int(page_size)), "pa_pool_release")
 
+    def refcount(self, page_id: int) -> int:
+        return int(lib().pa_pool_refcount(self._h, int(page_id)))
+
+    def share(self, ids):
+        import numpy as np
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        _check(lib().pa_pool_share(self._h, self._i32(ids) if ids.size else None, int(ids.size)),
+               "pa_pool_share")
+
+    def fork(self, src_row, dst_row, length: int, page_size: int = 16):
+        """dst_row starts as a sharer of src_row's pages for `length` keys."""
+        _check(lib().pa_pool_fork(self._h, self._i32(src_row), self._i32(dst_row), int(dst_row.size),
+                                  int(length), int(page_size)), "pa_pool_fork")
+
+    def cow(self, row, logical_page: int):
+        """Make logical page `logical_page` of `row` private before a write;
+        returns (old_id, new_id), equal when no copy is needed."""
+        old = ctypes.c_int32(-1)
+        new = ctypes.c_int32(-1)
+        _check(lib().pa_pool_cow(self._h, self._i32(row), int(row.size), int(logical_page),
+                                 ctypes.byref(old), ctypes.byref(new)), "pa_pool_cow")
+        return int(old.value), int(new.value)
+
 
 __all__ = ["pa_desc", "pa_plan_info", "PaError", "lib", "make_desc", "pa_plan",
            "pa_workspace_bytes", "pa_decode", "pa_split_merge", "pa_prefill_chunk",
            "pa_merge_partials", "pa_gather_kv", "pa_validate_metadata", "pa_status_str",
            "split_partials_view", "pa_append_kv", "bind_append_kv", "PagePool", "BoundCall",
-           "bind_decode", "bind_prefill_chunk", "EXPORTED"]
+           "bind_decode", "bind_prefill_chunk", "pa_copy_pages", "EXPORTED"]

@@ -448,6 +448,29 @@ pa_status pa_append_kv(const pa_desc* d, const void* k_new, const void* v_new,
                                                                                     : PA_ERR_HIP;
 }
 
+pa_status pa_copy_pages(const pa_desc* d, void* k_pool, void* v_pool, const int32_t* src_ids,
+                        const int32_t* dst_ids, int32_t n, void* stream) {
+  pa_status st = check_desc(d);
+  if (st != PA_OK) return st;
+  if (n < 0) return PA_ERR_ARG;
+  if (n == 0) return PA_OK;
+  if (!k_pool || !v_pool || !src_ids || !dst_ids) return PA_ERR_ARG;
+  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned4(src_ids) || !aligned4(dst_ids))
+    return PA_ERR_ARG;
+  pa::CopyPagesArgs a;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.src = src_ids;
+  a.dst = dst_ids;
+  a.n = n;
+  a.num_pages = d->num_pages;
+  a.page_bytes = (int64_t)d->num_kv_heads * d->page_size * d->head_dim * elem_bytes(d->dtype);
+  // enough workgroups to keep a few pages' copies spread over the chip
+  a.slices = (int32_t)((a.page_bytes / 16 + 1023) / 1024);
+  return pa::launch_copy_pages(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK
+                                                                                       : PA_ERR_HIP;
+}
+
 pa_status pa_merge_partials(int32_t rows, int32_t heads, int32_t num_splits, int32_t head_dim,
                             const float* o_part, const float* lse_part, void* out,
                             int32_t out_dtype, float* lse, void* stream) {

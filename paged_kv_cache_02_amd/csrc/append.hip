@@ -1,4 +1,5 @@
-// Append a step's new K and V rows into the paged KV cache (gfx950).
+// Append a step's new K and V rows into the paged KV cache, and copy whole
+// pages for a copy on write (gfx950).
 //
 // Every request's new tokens (a prefill chunk, or the one token of a decode
 // step) are written into the shared pool before attention reads them: token
@@ -81,9 +82,43 @@ __global__ void __launch_bounds__(kThreads) append_kernel(AppendArgs a) {
   }
 }
 
+// Copy whole pages (every KV head, K and V) from src[i] to dst[i]: the device
+// half of a copy on write, when a request about to write into a shared page
+// takes a private copy of it first.  One workgroup per (pair, slice of the
+// page); pairs naming a page outside [0, num_pages) are skipped.
+__global__ void __launch_bounds__(kThreads) copy_pages_kernel(CopyPagesArgs a) {
+  const int i = blockIdx.x / a.slices;
+  const int slice = blockIdx.x % a.slices;
+  const int src = a.src[i];
+  const int dst = a.dst[i];
+  if (src < 0 || src >= a.num_pages || dst < 0 || dst >= a.num_pages || src == dst) return;
+  const size_t chunks = a.page_bytes / 16;
+  const size_t per_slice = (chunks + a.slices - 1) / a.slices;
+  const size_t c0 = (size_t)slice * per_slice;
+  const size_t c1 = c0 + per_slice < chunks ? c0 + per_slice : chunks;
+  const uint4* __restrict__ ks = reinterpret_cast<const uint4*>(reinterpret_cast<const unsigned char*>(a.k_pool) + (size_t)src * a.page_bytes);
+  const uint4* __restrict__ vs = reinterpret_cast<const uint4*>(reinterpret_cast<const unsigned char*>(a.v_pool) + (size_t)src * a.page_bytes);
+  uint4* __restrict__ kd = reinterpret_cast<uint4*>(reinterpret_cast<unsigned char*>(a.k_pool) + (size_t)dst * a.page_bytes);
+  uint4* __restrict__ vd = reinterpret_cast<uint4*>(reinterpret_cast<unsigned char*>(a.v_pool) + (size_t)dst * a.page_bytes);
+#pragma unroll 4
+  for (size_t c = c0 + threadIdx.x; c < c1; c += kThreads) {
+    kd[c] = ks[c];
+    vd[c] = vs[c];
+  }
+}
+
 }  // namespace
 
 int append_rows_per_wg() { return kRowsPerWg; }
+
+hipError_t launch_copy_pages(const CopyPagesArgs& a, hipStream_t s) {
+  if (a.n <= 0) return hipSuccess;
+  if (a.page_bytes % 16 != 0 || a.slices < 1) return hipErrorInvalidValue;
+  const long long grid = (long long)a.n * a.slices;
+  if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(copy_pages_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
   const long long grid = (long long)a.num_seqs * a.tiles_per_seq;

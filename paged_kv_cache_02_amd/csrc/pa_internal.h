@@ -109,6 +109,19 @@ struct AppendArgs {
 int append_rows_per_wg();
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 
+// Whole-page copies (K and V, every KV head) from src[i] to dst[i].
+struct CopyPagesArgs {
+  void* k_pool;             // [NP, Hkv, P, d]
+  void* v_pool;
+  const int32_t* src;       // [n] page ids
+  const int32_t* dst;       // [n] page ids
+  int32_t n, num_pages;
+  int64_t page_bytes;       // Hkv * P * d * element size (a multiple of 16)
+  int32_t slices;           // workgroups per page
+};
+
+hipError_t launch_copy_pages(const CopyPagesArgs& a, hipStream_t s);
+
 // ---------------------------------------------------------------------------
 // page gather (test hook)
 // ---------------------------------------------------------------------------

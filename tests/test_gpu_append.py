@@ -136,3 +136,102 @@ def test_serving_sequence_allocator_append_attention():
             lens[1] = 0
             prompts[1] = 90
     assert pool.num_free == NP - sum(int((table[r] >= 0).sum()) for r in range(3))
+
+
+@pytest.mark.parametrize("Hkv,d,dtype", [(8, 128, W.BF16), (2, 64, W.F32)])
+def test_copy_pages_matches_oracle_bit_exact(Hkv, d, dtype):
+    rng = np.random.default_rng(31)
+    NP, P = 40, 16
+    if dtype == W.BF16:
+        kp = W.f32_to_bf16_bits(rng.standard_normal((NP, Hkv, P, d)).astype(np.float32))
+        vp = W.f32_to_bf16_bits(rng.standard_normal((NP, Hkv, P, d)).astype(np.float32))
+    else:
+        kp = rng.standard_normal((NP, Hkv, P, d)).astype(np.float32)
+        vp = rng.standard_normal((NP, Hkv, P, d)).astype(np.float32)
+    src = np.array([3, 17, 0, 25, 39, 12, -1, 8], np.int32)
+    dst = np.array([30, 1, 22, 5, 36, 12, 9, 99], np.int32)   # a self-copy and two bad pairs
+    kt, vt = to_torch(kp, dtype), to_torch(vp, dtype)
+    desc = pa.pa_desc(1, Hkv, Hkv, d, P, NP, 4, 1, P, 1, pa.PA_BF16 if dtype == W.BF16 else pa.PA_F32)
+    pa.pa_copy_pages(kt, vt, torch.from_numpy(src).cuda(), torch.from_numpy(dst).cuda(), desc=desc)
+    torch.cuda.synchronize()
+    k2, v2 = ORACLE.copy_pages(kp, vp, src, dst)
+    assert np.array_equal(raw(kt).view(np.uint8), k2.view(np.uint8))
+    assert np.array_equal(raw(vt).view(np.uint8), v2.view(np.uint8))
+
+
+def test_shared_prefix_pages_with_copy_on_write():
+    """Request A prefills a 70-token prompt; B and C fork A's first 70 keys
+    (five pages: four full and one partial) and then decode and append their
+    own tokens.  The first append into the shared partial page takes a
+    private copy (pool.cow + pa_copy_pages), so A's cache never changes under
+    it.  Every step's attention for all three requests matches the oracle on
+    the oracle's own copy of the pools, and A's prefix pages stay shared."""
+    rng = np.random.default_rng(8)
+    Hq, Hkv, d, P = 8, 2, 128, 16
+    NP, MP = 32, 12
+    pool = pa.PagePool(NP)
+    k_pool = torch.zeros(NP, Hkv, P, d, dtype=torch.bfloat16, device="cuda")
+    v_pool = torch.zeros_like(k_pool)
+    kp_host = np.zeros((NP, Hkv, P, d), np.uint16)
+    vp_host = np.zeros_like(kp_host)
+    table = np.full((3, MP), -1, np.int32)
+    scale = 1.0 / np.sqrt(d)
+    desc_copy = pa.pa_desc(1, Hkv, Hkv, d, P, NP, MP, 1, P, 1, pa.PA_BF16)
+
+    def step(active, lens, n, label):
+        nonlocal kp_host, vp_host
+        rows = int(sum(n))
+        offs = np.array(lens, np.int64)
+        new = offs + np.array(n, np.int64)
+        kn = W.f32_to_bf16_bits(rng.standard_normal((rows, Hkv, d)).astype(np.float32))
+        vn = W.f32_to_bf16_bits(rng.standard_normal((rows, Hkv, d)).astype(np.float32))
+        q = W.f32_to_bf16_bits(rng.standard_normal((rows, Hq, d)).astype(np.float32))
+        t = table[active].copy()
+        sl = torch.from_numpy(new.astype(np.int32)).cuda()
+        qo = torch.from_numpy(offs.astype(np.int32)).cuda()
+        pt = torch.from_numpy(t).cuda()
+        pa.pa_append_kv(to_torch(kn, W.BF16), to_torch(vn, W.BF16), k_pool, v_pool, pt, sl, qo,
+                        max_seq_len=int(new.max()), max_q_len=int(max(n)))
+        kp_host, vp_host = ORACLE.append_kv(kp_host, vp_host, t, new, offs, kn, vn)
+        qt = to_torch(q, W.BF16)
+        if max(n) > 1:
+            out, lse = pa.pa_prefill_chunk(qt, k_pool, v_pool, pt, sl, qo, scale,
+                                           max_seq_len=int(new.max()), max_q_len=int(max(n)))
+        else:
+            out, lse = pa.pa_decode(qt, k_pool, v_pool, pt, sl, qo, scale, max_seq_len=int(new.max()))
+        torch.cuda.synchronize()
+        assert np.array_equal(raw(k_pool).view(np.uint8), kp_host.view(np.uint8))
+        assert np.array_equal(raw(v_pool).view(np.uint8), vp_host.view(np.uint8))
+        b = W.PagedBatch(name=label, seed=0, q=q, k_pool=kp_host, v_pool=vp_host, page_table=t,
+                         seq_lens=new.astype(np.int32), q_offsets=offs.astype(np.int32), num_q_heads=Hq,
+                         num_kv_heads=Hkv, head_dim=d, page_size=P, scale=scale, dtype=W.BF16)
+        ro, rl = oracle_run(b)
+        compare(b, out, lse, ro, rl, label=label)
+        return [int(x) for x in new]
+
+    # A prefills its prompt
+    pool.reserve(table[0], 0, 70, P)
+    (len_a,) = step([0], [0], [70], "A prompt")
+    prefix_pages = table[0, :5].copy()
+    a_prefix_k = raw(k_pool)[prefix_pages].copy()
+    # B and C start from A's prefix
+    pool.fork(table[0], table[1], 70, P)
+    pool.fork(table[0], table[2], 70, P)
+    assert [pool.refcount(i) for i in prefix_pages] == [3] * 5
+    lens = [len_a, 70, 70]
+    for it in range(20):
+        for r in (1, 2, 0):
+            lp = lens[r] // P                      # the page this request writes next
+            if lp < MP and table[r, lp] >= 0:
+                old, new = pool.cow(table[r], lp)
+                if old != new:                     # shared: copy before writing
+                    pa.pa_copy_pages(k_pool, v_pool, torch.tensor([old], dtype=torch.int32, device="cuda"),
+                                     torch.tensor([new], dtype=torch.int32, device="cuda"), desc=desc_copy)
+                    kp_host, vp_host = ORACLE.copy_pages(kp_host, vp_host, [old], [new])
+            pool.reserve(table[r], lens[r], lens[r] + 1, P)
+        lens = step([0, 1, 2], lens, [1, 1, 1], f"decode {it}")
+    # the full prefix pages are still shared by all three; the partial one was copied
+    assert [pool.refcount(i) for i in prefix_pages[:4]] == [3] * 4
+    assert table[1, 4] != prefix_pages[4] and table[2, 4] != prefix_pages[4]
+    # A's own appends went into its partial page 4 and beyond, never into B's or C's copies
+    assert np.array_equal(raw(k_pool)[prefix_pages[:4]], a_prefix_k[:4])

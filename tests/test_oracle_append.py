@@ -150,3 +150,82 @@ def test_mutants_are_caught(name):
         except Exception:   # assertion or crash both count as caught
             caught.append(pin.__name__)
     assert caught, f"mutant {name} passed every pin"
+
+
+# ---- copy_pages (the device half of a copy on write) ----
+
+def _copy_case(seed):
+    rng = np.random.default_rng(seed)
+    NP, Hkv, P, d = 12, 3, 4, 8
+    kp = rng.standard_normal((NP, Hkv, P, d)).astype(np.float32)
+    vp = rng.standard_normal((NP, Hkv, P, d)).astype(np.float32)
+    src = np.array([3, 7, 0], np.int32)
+    dst = np.array([10, 2, 5], np.int32)
+    return kp, vp, src, dst
+
+
+def cpin_gather_through_copy(mod):
+    kp, vp, src, dst = _copy_case(21)
+    k2, v2 = mod.copy_pages(kp, vp, src, dst)
+    P = kp.shape[2]
+    # a request whose table names the source pages, and the same request
+    # with the copies in their place, gather the same keys and values
+    t_src = np.array(src, np.int32)
+    t_dst = np.array(dst, np.int32)
+    L = len(src) * P - 1
+    Ks, Vs = ORACLE.gather(k2, v2, t_src, L)
+    Kd, Vd = ORACLE.gather(k2, v2, t_dst, L)
+    assert np.array_equal(Ks, Kd) and np.array_equal(Vs, Vd)
+    K0, V0 = ORACLE.gather(kp, vp, t_src, L)
+    assert np.array_equal(Kd, K0) and np.array_equal(Vd, V0)
+
+
+def cpin_other_pages_untouched(mod):
+    kp, vp, src, dst = _copy_case(22)
+    k2, v2 = mod.copy_pages(kp, vp, src, dst)
+    for page in range(kp.shape[0]):
+        if page not in dst:
+            assert np.array_equal(k2[page], kp[page]) and np.array_equal(v2[page], vp[page])
+    kp0, vp0, *_ = _copy_case(22)
+    assert np.array_equal(kp, kp0) and np.array_equal(vp, vp0)
+
+
+def cpin_bad_pairs_are_skipped(mod):
+    kp, vp, _, _ = _copy_case(23)
+    k2, v2 = mod.copy_pages(kp, vp, np.array([4, -1, 99, 6], np.int32), np.array([4, 2, 3, -5], np.int32))
+    assert np.array_equal(k2, kp) and np.array_equal(v2, vp)
+
+
+CPINS = [cpin_gather_through_copy, cpin_other_pages_untouched, cpin_bad_pairs_are_skipped]
+
+
+@pytest.mark.parametrize("pin", CPINS, ids=lambda p: p.__name__)
+def test_copy_pin(pin):
+    pin(KVA)
+
+
+COPY_MUTANTS = {
+    "direction_swapped": ("k_out[d_id] = k_pool[s_id]", "k_out[s_id] = k_pool[d_id]"),
+    "v_from_k": ("v_out[d_id] = v_pool[s_id]", "v_out[d_id] = k_pool[s_id]"),
+    "one_head_only": ("k_out[d_id] = k_pool[s_id]", "k_out[d_id, 0] = k_pool[s_id, 0]"),
+    "no_skip_checks": ("if not (0 <= s_id < num_pages and 0 <= d_id < num_pages) or s_id == d_id:",
+                       "if False:"),
+    "in_place": ("k_out = k_pool.copy()\n    v_out = v_pool.copy()\n    num_pages",
+                 "k_out = k_pool\n    v_out = v_pool.copy()\n    num_pages"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(COPY_MUTANTS))
+def test_copy_mutants_are_caught(name):
+    src = open(KVA.__file__).read()
+    old, new = COPY_MUTANTS[name]
+    assert src.count(old) >= 1, old
+    mod = types.ModuleType("kv_copy_mutant")
+    exec(compile(src.replace(old, new, 1), "kv_copy_mutant", "exec"), mod.__dict__)
+    caught = []
+    for pin in CPINS:
+        try:
+            pin(mod)
+        except Exception:
+            caught.append(pin.__name__)
+    assert caught, f"mutant {name} passed every pin"

@@ -106,3 +106,88 @@ def test_null_and_invalid_arguments():
     h = ctypes.c_void_p()
     assert L.pa_pool_create(0, ctypes.byref(h)) == pa.PA_ERR_ARG
     assert L.pa_pool_create(4, None) == pa.PA_ERR_ARG
+
+
+# ---- shared pages: reference counts, fork, copy on write ----
+
+def test_shared_page_returns_to_the_pool_after_its_last_holder():
+    pool = pa.PagePool(6)
+    a = pool.alloc(2)
+    assert pool.refcount(a[0]) == 1
+    pool.share(a)                       # a second holder of both pages
+    assert pool.refcount(a[0]) == 2 and pool.refcount(a[1]) == 2
+    pool.free(a)
+    assert pool.num_free == 4 and pool.refcount(a[0]) == 1
+    pool.free(a)
+    assert pool.num_free == 6 and pool.refcount(a[0]) == 0
+    assert pool.refcount(99) == -1
+
+
+def test_free_may_list_a_page_as_often_as_it_is_held():
+    pool = pa.PagePool(4)
+    a = pool.alloc(1)
+    pool.share(a)
+    with pytest.raises(pa.PaError):
+        pool.free(np.array([a[0]] * 3, np.int32))   # held twice, listed three times
+    assert pool.refcount(a[0]) == 2
+    pool.free(np.array([a[0], a[0]], np.int32))
+    assert pool.refcount(a[0]) == 0 and pool.num_free == 4
+
+
+def test_share_rejects_free_or_out_of_range_pages_without_side_effects():
+    pool = pa.PagePool(4)
+    a = pool.alloc(1)
+    for bad in ([a[0], 3 if a[0] != 3 else 2], [-1], [4]):
+        with pytest.raises(pa.PaError) as e:
+            pool.share(np.array(bad, np.int32))
+        assert e.value.code == pa.PA_ERR_ARG
+    assert pool.refcount(a[0]) == 1
+
+
+def test_fork_shares_a_prefix_and_release_drops_one_reference():
+    P, MP = 16, 8
+    pool = pa.PagePool(10)
+    src = np.full(MP, -1, np.int32)
+    pool.reserve(src, 0, 40, P)                        # 3 pages
+    dst = np.full(MP, -1, np.int32)
+    pool.fork(src, dst, 40, P)
+    assert np.array_equal(dst[:3], src[:3]) and (dst[3:] == -1).all()
+    assert [pool.refcount(i) for i in src[:3]] == [2, 2, 2]
+    assert pool.num_free == 7
+    pool.release(src, 40, P)
+    assert (src[:3] == -1).all() and [pool.refcount(i) for i in dst[:3]] == [1, 1, 1]
+    assert pool.num_free == 7                          # still held by dst
+    pool.release(dst, 40, P)
+    assert pool.num_free == 10
+
+
+def test_cow_copies_only_shared_pages():
+    P, MP = 16, 8
+    pool = pa.PagePool(10)
+    a = np.full(MP, -1, np.int32)
+    pool.reserve(a, 0, 40, P)
+    b = np.full(MP, -1, np.int32)
+    pool.fork(a, b, 40, P)
+    old, new = pool.cow(b, 2)                          # b is about to append into page 2
+    assert old == a[2] and new != old and b[2] == new
+    assert pool.refcount(old) == 1 and pool.refcount(new) == 1
+    assert np.array_equal(b[:2], a[:2])                # the full prefix pages stay shared
+    same = pool.cow(b, 2)                              # now private: no further copy
+    assert same == (new, new)
+    old_a, new_a = pool.cow(a, 2)                      # a is again the only holder
+    assert old_a == new_a == a[2]
+
+
+def test_cow_without_a_free_page_changes_nothing():
+    P, MP = 16, 4
+    pool = pa.PagePool(3)
+    a = np.full(MP, -1, np.int32)
+    pool.reserve(a, 0, 48, P)                          # all 3 pages
+    b = np.full(MP, -1, np.int32)
+    pool.fork(a, b, 48, P)
+    with pytest.raises(pa.PaError) as e:
+        pool.cow(b, 1)
+    assert e.value.code == pa.PA_ERR_NO_PAGES
+    assert np.array_equal(a[:3], b[:3]) and pool.refcount(b[1]) == 2
+    with pytest.raises(pa.PaError):
+        pool.cow(b, 3)                                 # an empty entry is not a held page
