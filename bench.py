@@ -23,6 +23,7 @@ from the 256 MB last-level cache.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -49,10 +50,13 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0,
                     help="wall-clock budget of the oracle's CPU baseline sample")
-    ap.add_argument("--mode", choices=("step", "copy"), default="step",
+    ap.add_argument("--mode", choices=("step", "copy", "baselines"), default="step",
                     help="step: the benchmark; copy: calibration of the HBM counters and "
                          "the streaming ceiling (a plain 1 GiB device copy and a read-only "
-                         "reduction of known size)")
+                         "reduction of known size); baselines: the Qwen3-4B-shaped decode "
+                         "through the production route, the same fused kernel unsplit over "
+                         "pages and over a dense cache, and direct (non-flash) paged "
+                         "attention")
     return ap.parse_args()
 
 
@@ -81,6 +85,76 @@ def copy_calibration(steps: int):
         us = e0.elapsed_time(e1) * 1e3 / steps
         res[name] = {"us": round(us, 2), "GB/s": round(nbytes / us / 1e3, 1), "bytes": nbytes}
     print(json.dumps({"calibration": res}), flush=True)
+
+
+def baselines(steps: int, warmup: int):
+    """What paging and the online softmax cost: the Qwen3-4B-shaped decode
+    config (64 requests, 32/8 heads, d = 128, contexts in [1024, 8192]) timed
+    through (1) pa_decode (the guard's balanced route), (2) the fused
+    per-(request, KV head) kernel unsplit over the pages (pa_split_merge with
+    one split: its merge pass is timed with it), (3) the same fused kernel
+    over a dense cache (pa_decode_dense) and (4) direct paged attention with
+    stored scores (pa_decode_direct).  One JSON line: microseconds per call
+    and algorithmic GB/s (the K/V bytes and metadata every variant must
+    read)."""
+    import torch
+    import paged_kv_cache_02_amd as pa
+    import workloads as W
+    b = W.make_config("qwen3_4b_decode", poison=False)
+    dev = torch.device("cuda:0")
+
+    def to_dev(arr):
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+    q, kp, vp = to_dev(b.q), to_dev(b.k_pool), to_dev(b.v_pool)
+    pt, sl, qo = i32(b.page_table), i32(b.seq_lens), i32(b.q_offsets)
+    B, MP, P = b.num_seqs, b.page_table.shape[1], b.page_size
+    # the dense cache [B, Hkv, MP * P, d]: each request's pages laid end to end
+    kd = np.zeros((B, b.num_kv_heads, MP * P, b.head_dim), np.uint16)
+    vd = np.zeros_like(kd)
+    for r in range(B):
+        L = int(b.seq_lens[r])
+        n = (L + P - 1) // P
+        pages = b.page_table[r, :n]
+        kd[r, :, :n * P] = b.k_pool[pages].transpose(1, 0, 2, 3).reshape(b.num_kv_heads, n * P, -1)
+        vd[r, :, :n * P] = b.v_pool[pages].transpose(1, 0, 2, 3).reshape(b.num_kv_heads, n * P, -1)
+        kd[r, :, L:] = 0
+        vd[r, :, L:] = 0
+    kdt, vdt = to_dev(kd), to_dev(vd)
+    del kd, vd
+    desc = pa.make_desc(q, kp, pt, sl, b.max_seq_len, 1)
+    out = torch.empty_like(q)
+    lse = torch.empty(B, b.num_q_heads, dtype=torch.float32, device=dev)
+    ws_dec = torch.empty(max(pa.pa_plan(desc)["workspace_bytes"], 256), dtype=torch.uint8, device=dev)
+    ws_split = torch.empty(max(pa.pa_workspace_bytes(desc, 1), 256), dtype=torch.uint8, device=dev)
+    ws_direct = torch.empty(max(int(pa.lib().pa_direct_workspace_bytes(ctypes.byref(desc))), 256),
+                            dtype=torch.uint8, device=dev)
+    variants = {
+        "paged_balanced": lambda: pa.pa_decode(q, kp, vp, pt, sl, qo, b.scale, out=out, lse=lse,
+                                               workspace=ws_dec, desc=desc),
+        "paged_unsplit": lambda: pa.pa_split_merge(q, kp, vp, pt, sl, qo, b.scale, 1, out=out, lse=lse,
+                                                   workspace=ws_split, desc=desc),
+        "dense_unsplit": lambda: pa.pa_decode_dense(q, kdt, vdt, sl, b.scale, desc=desc, out=out, lse=lse),
+        "direct_paged": lambda: pa.pa_decode_direct(q, kp, vp, pt, sl, b.scale, desc=desc, out=out, lse=lse,
+                                                    workspace=ws_direct),
+    }
+    nbytes = decode_alg_bytes(b)
+    res = {}
+    for name, fn in variants.items():
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        res[name] = {"us": round(us, 1), "GB/s": round(nbytes / us / 1e3, 1)}
+        print(f"{name}: {res[name]}", file=sys.stderr, flush=True)
+    print(json.dumps({"baselines": res, "workload": "qwen3_4b_decode", "alg_bytes": nbytes}), flush=True)
 
 
 def source_hash(*names) -> str:
@@ -192,6 +266,9 @@ def main():
 
     if args.mode == "copy":
         copy_calibration(args.steps)
+        return
+    if args.mode == "baselines":
+        baselines(args.steps, args.warmup)
         return
     torch.cuda.init()
     dev = torch.device("cuda:0")

@@ -154,6 +154,30 @@ pa_status pa_split_merge(const pa_desc* desc, const void* q, const void* k_pool,
                          void* workspace, size_t workspace_bytes, void* out, float* lse,
                          void* stream);
 
+/* Baselines for measuring what paging and online softmax cost (same row
+ * contract and outputs as pa_decode; bf16 or fp32, d = 64 or 128, G in
+ * {1, 2, 4, 8}):
+ *   pa_decode_dense:  the same fused (online-softmax) per-(request, KV head)
+ *                     kernel over a dense cache k_cache, v_cache
+ *                     [B, Hkv, MP * P, d] (MP = desc->max_pages_per_seq, the
+ *                     capacity in pages; request r's first seq_lens[r] keys
+ *                     of each KV head are contiguous), with no page table:
+ *                     the dense KV cache the pages start from ("Build a vLLM
+ *                     from Scratch", Week 2) before paging (Week 3).
+ *   pa_decode_direct: attention read through the page table but not fused:
+ *                     every score is stored (fp32) in `workspace` (at least
+ *                     pa_direct_workspace_bytes(desc) = B * Hq * MP * P * 4
+ *                     bytes), each head's row is turned into softmax weights
+ *                     in place, then the values are summed: the direct paged
+ *                     attention that "Build a vLLM from Scratch", Week 3,
+ *                     names next to Paged FlashAttention. */
+pa_status pa_decode_dense(const pa_desc* desc, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* seq_lens, float scale, void* out, float* lse, void* stream);
+size_t pa_direct_workspace_bytes(const pa_desc* desc);
+pa_status pa_decode_direct(const pa_desc* desc, const void* q, const void* k_pool, const void* v_pool,
+                           const int32_t* page_table, const int32_t* seq_lens, float scale, void* out,
+                           float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Chunked prefill: request r's n_r query rows (a chunk of a prompt at prior
  * offset q_offsets[r]) attend causally to keys 0 .. q_offsets[r] + i, all of
  * them read from the pages (the chunk's own K/V already appended).  bf16

@@ -75,6 +75,10 @@ _SIGS = {
     "pa_pool_fork": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]),
     "pa_pool_cow": (ctypes.c_int, [_P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P]),
     "pa_copy_pages": (ctypes.c_int, [_D, _P, _P, _P, _P, ctypes.c_int32, _P]),
+    "pa_decode_dense": (ctypes.c_int, [_D, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P]),
+    "pa_direct_workspace_bytes": (ctypes.c_size_t, [_D]),
+    "pa_decode_direct": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P,
+                                        ctypes.c_size_t, _P]),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -187,6 +191,31 @@ def pa_decode(q, k_pool, v_pool, page_table, seq_lens, q_offsets, scale, *,
                            _ptr(page_table), _ptr(seq_lens), _ptr(q_offsets), float(scale),
                            _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(q.device)),
            "pa_decode")
+    return out, lse
+
+
+def pa_decode_dense(q, k_cache, v_cache, seq_lens, scale, *, desc, out=None, lse=None):
+    """Decode over a dense cache [B, Hkv, MP * P, d] (no page table; MP =
+    desc.max_pages_per_seq); returns (out, lse)."""
+    out, lse = _alloc_out(q, out, lse)
+    _check(lib().pa_decode_dense(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                 _ptr(seq_lens), float(scale), _ptr(out), _ptr(lse), _stream(q.device)),
+           "pa_decode_dense")
+    return out, lse
+
+
+def pa_decode_direct(q, k_pool, v_pool, page_table, seq_lens, scale, *, desc, out=None, lse=None,
+                     workspace=None):
+    """Decode through the page table without the flash fusion (scores stored,
+    softmax, then values); returns (out, lse)."""
+    out, lse = _alloc_out(q, out, lse)
+    need = int(lib().pa_direct_workspace_bytes(ctypes.byref(desc)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().pa_decode_direct(ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                  _ptr(page_table), _ptr(seq_lens), float(scale), _ptr(out), _ptr(lse),
+                                  _ptr(workspace), ws_bytes, _stream(q.device)), "pa_decode_direct")
     return out, lse
 
 
@@ -422,4 +451,5 @@ __all__ = ["pa_desc", "pa_plan_info", "PaError", "lib", "make_desc", "pa_plan",
            "pa_workspace_bytes", "pa_decode", "pa_split_merge", "pa_prefill_chunk",
            "pa_merge_partials", "pa_gather_kv", "pa_validate_metadata", "pa_status_str",
            "split_partials_view", "pa_append_kv", "bind_append_kv", "PagePool", "BoundCall",
-           "bind_decode", "bind_prefill_chunk", "pa_copy_pages", "EXPORTED"]
+           "bind_decode", "bind_prefill_chunk", "pa_copy_pages", "pa_decode_dense",
+           "pa_decode_direct", "EXPORTED"]

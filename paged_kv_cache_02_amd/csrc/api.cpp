@@ -339,6 +339,57 @@ pa_status pa_decode(const pa_desc* d, const void* q, const void* k_pool, const v
   return run_split(d, a, plan.num_splits, workspace, out, lse, s);
 }
 
+pa_status pa_decode_dense(const pa_desc* d, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* seq_lens, float scale, void* out, float* lse, void* stream) {
+  // the page-table check is satisfied with seq_lens: the dense kernel reads no table
+  pa_status st = check_decode_call(d, q, k_cache, v_cache, seq_lens, seq_lens, scale, out, lse);
+  if (st != PA_OK || d->num_seqs == 0) return st;
+  pa::DecodeArgs a = decode_args(d, q, k_cache, v_cache, nullptr, seq_lens, scale);
+  a.out = out;
+  a.lse = lse;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  return pa::launch_decode_dense(a, d->dtype, d->head_dim, G, reinterpret_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? PA_OK
+             : PA_ERR_HIP;
+}
+
+size_t pa_direct_workspace_bytes(const pa_desc* d) {
+  if (check_desc(d) != PA_OK) return 0;
+  return align_up((size_t)d->num_seqs * d->num_q_heads * d->max_pages_per_seq * d->page_size *
+                  sizeof(float));
+}
+
+pa_status pa_decode_direct(const pa_desc* d, const void* q, const void* k_pool, const void* v_pool,
+                           const int32_t* page_table, const int32_t* seq_lens, float scale, void* out,
+                           float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  pa_status st = check_decode_call(d, q, k_pool, v_pool, page_table, seq_lens, scale, out, lse);
+  if (st != PA_OK || d->num_seqs == 0) return st;
+  if (workspace == nullptr || workspace_bytes < pa_direct_workspace_bytes(d) || !aligned16(workspace))
+    return PA_ERR_WORKSPACE;
+  pa::DirectArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.page_table = page_table;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.lse = lse;
+  a.scores = reinterpret_cast<float*>(workspace);
+  a.num_seqs = d->num_seqs;
+  a.num_q_heads = d->num_q_heads;
+  a.num_kv_heads = d->num_kv_heads;
+  a.max_pages_per_seq = d->max_pages_per_seq;
+  a.num_pages = d->num_pages;
+  a.scale_log2 = scale * kLog2e;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  return pa::launch_decode_direct(a, d->dtype, d->head_dim, G, reinterpret_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? PA_OK
+             : PA_ERR_HIP;
+}
+
 pa_status pa_split_merge(const pa_desc* d, const void* q, const void* k_pool, const void* v_pool,
                          const int32_t* page_table, const int32_t* seq_lens,
                          const int32_t* q_offsets, float scale, int32_t num_splits,

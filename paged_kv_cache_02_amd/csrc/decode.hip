@@ -344,7 +344,10 @@ struct Pipe {
   static constexpr int kBufs = kDepth + 1;
 };
 
-template <typename T, int D, int G>
+// kDense: the same kernel over a dense cache [B, Hkv, MP * P, d] (request
+// r's keys of KV head g contiguous, no page table), for measuring what the
+// paging costs; a.max_pages_per_seq is then the cache capacity in pages.
+template <typename T, int D, int G, bool kDense>
 __global__ void __launch_bounds__(kThreads)
 decode_kernel(DecodeArgs a) {
   using S = Shape<T, D, G>;
@@ -375,7 +378,7 @@ decode_kernel(DecodeArgs a) {
   const T* __restrict__ qp = reinterpret_cast<const T*>(a.q);
   const T* __restrict__ kpool = reinterpret_cast<const T*>(a.k_pool);
   const T* __restrict__ vpool = reinterpret_cast<const T*>(a.v_pool);
-  const int32_t* __restrict__ ptab = a.page_table + (size_t)r * a.max_pages_per_seq;
+  const int32_t* __restrict__ ptab = kDense ? nullptr : a.page_table + (size_t)r * a.max_pages_per_seq;
 
   // q chunks of the lane's dims for every head of the group
   uint4 qv[G][S::kChunksPerLane];
@@ -394,10 +397,12 @@ decode_kernel(DecodeArgs a) {
   const int nw = first < pe ? (pe - first + kWaves - 1) / kWaves : 0;
   auto page_id = [&](int i) -> int {  // clamped index: always a valid entry
     const int ic = i < nw ? i : nw - 1;
+    if (kDense) return first + kWaves * ic;
     int phys = ptab[first + kWaves * ic];
     return phys < 0 ? 0 : (phys >= num_pages ? num_pages - 1 : phys);
   };
   auto block_ptr = [&](const T* pool, int phys) -> const T* {
+    if (kDense) return pool + (((size_t)r * Hkv + g) * a.max_pages_per_seq + phys) * blk;
     return pool + ((size_t)phys * Hkv + g) * blk;
   };
 
@@ -739,12 +744,12 @@ decode_balanced_kernel(DecodeArgs a, const int32_t* __restrict__ page_table,
   }
 }
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool kDense>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
   const long long grid = (long long)a.num_seqs * a.num_kv_heads * a.num_splits;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((decode_kernel<T, D, G>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((decode_kernel<T, D, G, kDense>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -770,13 +775,13 @@ hipError_t launch_bal_g(const DecodeArgs& a, int group, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-template <typename T, int D>
+template <typename T, int D, bool kDense>
 hipError_t launch_g(const DecodeArgs& a, int group, hipStream_t s) {
   switch (group) {
-    case 1: return launch_t<T, D, 1>(a, s);
-    case 2: return launch_t<T, D, 2>(a, s);
-    case 4: return launch_t<T, D, 4>(a, s);
-    case 8: return launch_t<T, D, 8>(a, s);
+    case 1: return launch_t<T, D, 1, kDense>(a, s);
+    case 2: return launch_t<T, D, 2, kDense>(a, s);
+    case 4: return launch_t<T, D, 4, kDense>(a, s);
+    case 8: return launch_t<T, D, 8, kDense>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -801,11 +806,23 @@ hipError_t launch_decode_balanced(const DecodeArgs& a, int dtype, int head_dim, 
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int group, hipStream_t s) {
   if (dtype == 0) {
-    if (head_dim == 128) return launch_g<__bf16, 128>(a, group, s);
-    if (head_dim == 64) return launch_g<__bf16, 64>(a, group, s);
+    if (head_dim == 128) return launch_g<__bf16, 128, false>(a, group, s);
+    if (head_dim == 64) return launch_g<__bf16, 64, false>(a, group, s);
   } else if (dtype == 1) {
-    if (head_dim == 128) return launch_g<float, 128>(a, group, s);
-    if (head_dim == 64) return launch_g<float, 64>(a, group, s);
+    if (head_dim == 128) return launch_g<float, 128, false>(a, group, s);
+    if (head_dim == 64) return launch_g<float, 64, false>(a, group, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_dense(const DecodeArgs& a, int dtype, int head_dim, int group, hipStream_t s) {
+  if (a.num_splits != 1 || a.write_partials) return hipErrorInvalidValue;
+  if (dtype == 0) {
+    if (head_dim == 128) return launch_g<__bf16, 128, true>(a, group, s);
+    if (head_dim == 64) return launch_g<__bf16, 64, true>(a, group, s);
+  } else if (dtype == 1) {
+    if (head_dim == 128) return launch_g<float, 128, true>(a, group, s);
+    if (head_dim == 64) return launch_g<float, 64, true>(a, group, s);
   }
   return hipErrorInvalidValue;
 }

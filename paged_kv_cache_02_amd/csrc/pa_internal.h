@@ -39,10 +39,31 @@ struct DecodeArgs {
 // dtype: 0 = bf16, 1 = fp32.  Returns hipSuccess or the launch error.
 bool decode_group_supported(int group);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int group, hipStream_t s);
+// The per-(request, KV head) kernel over a dense cache [B, Hkv, MP * P, d]
+// (a.page_table unused; a.max_pages_per_seq = capacity in pages; unsplit).
+hipError_t launch_decode_dense(const DecodeArgs& a, int dtype, int head_dim, int group, hipStream_t s);
 // Page-balanced split: every KV head's flattened (request, page) sequence is
 // cut into a.num_splits equal wave ranges (a.num_splits a multiple of 4).
 hipError_t launch_decode_balanced(const DecodeArgs& a, int dtype, int head_dim, int group,
                                   hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// direct (non-flash) paged decode: scores stored, then softmax, then values
+// ---------------------------------------------------------------------------
+struct DirectArgs {
+  const void* q;            // [B, Hq, d]
+  const void* k_pool;       // [NP, Hkv, P, d]
+  const void* v_pool;
+  const int32_t* page_table;  // [B, MP]
+  const int32_t* seq_lens;    // [B]
+  void* out;                // [B, Hq, d]
+  float* lse;               // [B, Hq] or null
+  float* scores;            // scratch [B, Hq, MP * P] fp32
+  int32_t num_seqs, num_q_heads, num_kv_heads, max_pages_per_seq, num_pages;
+  float scale_log2;
+};
+
+hipError_t launch_decode_direct(const DirectArgs& a, int dtype, int head_dim, int group, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // log-sum-exp merge of split partials
