@@ -367,8 +367,54 @@ def main():
     dec_gbs = dec_bytes / (dc_ms * 1e-3) / 1e9
     pf_tflops = pf_flops / (pf_ms * 1e-3) / 1e12
 
-    pf_hash = source_hash("prefill.hip")
-    dc_hash = source_hash("decode.hip", "merge.hip")
+    # the same step with attention as one mixed launch (pa_mixed_attention:
+    # the chunks' row tiles and the decode (request, KV head) items in one
+    # grid, no merge pass), timed the same way
+    mx_q = to_dev(full.q, full.dtype)
+    mx_out = torch.empty_like(mx_q)
+    mx_lse = torch.empty(full.total_q, full.num_q_heads, dtype=torch.float32, device=dev)
+    mx_desc = pa.make_desc(mx_q, pools[0][0], full_t["pt"], full_t["sl"], full.max_seq_len,
+                           full.max_q_len)
+    for i in (0, 1):
+        kp, vp = pools[i]
+        calls[("mixed", i)] = pa.bind_mixed_attention(
+            mx_q, kp, vp, full_t["pt"], full_t["sl"], full_t["qo"], full.scale,
+            q_starts=full_t["qs"], out=mx_out, lse=mx_lse, desc=mx_desc)
+
+    def step_single(i, ev=None):
+        if ev is not None:
+            ev[0].record()
+        calls[("append", i & 1)]()
+        if ev is not None:
+            ev[1].record()
+        calls[("mixed", i & 1)]()
+        if ev is not None:
+            ev[2].record()
+
+    for i in range(args.warmup):
+        step_single(i)
+    torch.cuda.synchronize()
+    evm = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step_single(i, evm[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    mx_step_ms = (t1 - t0) * 1e3 / args.steps
+    mx_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evm]))
+    single = {
+        "ms_per_step": round(mx_step_ms, 4), "attention_ms": round(mx_ms, 4),
+        "kernel": "mixed_kernel<128,4>",
+        "traffic": load_traffic("mixed", source_hash("mixed.hip", "prefill_core.h", "decode_core.h")),
+        "attention_ms_separate_routes": round(pf_ms + dc_ms, 4),
+        "speedup_vs_separate_routes": round((pf_ms + dc_ms) / mx_ms, 3),
+        # the share of each roofline the one launch reaches over its own time
+        "hbm_frac": round(dec_bytes / (mx_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "mfma_frac": round(pf_flops / (mx_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+    }
+
+    pf_hash = source_hash("prefill.hip", "prefill_core.h")
+    dc_hash = source_hash("decode.hip", "decode_core.h", "merge.hip")
     kernels = {
         "prefill": {"bound": "mfma", "achieved": round(pf_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(pf_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
@@ -416,6 +462,7 @@ def main():
         "prefill_frac_of_mfma_peak": round(pf_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "decode_frac_of_hbm_peak": round(dec_gbs / HBM_PEAK_GBS, 4),
         "kernels": kernels,
+        "single_launch": single,
         "roofline": roof,
         "cpu_baseline": None,
     }

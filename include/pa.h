@@ -194,6 +194,29 @@ pa_status pa_prefill_chunk(const pa_desc* desc, const void* q, const void* k_poo
                            void* out, float* lse, void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/* Mixed batch in one launch: one continuous-batching round whose requests
+ * are in either phase (the tiny-llm source reading, "Continuous Batching":
+ * one round carries prefill and decode requests side by side).  Request r
+ * has n_r = seq_lens[r] - q_offsets[r] query rows, packed like
+ * pa_prefill_chunk's q (q_starts as there, or NULL); n_r = 1 rows are
+ * decoded and n_r > 1 chunks are prefilled, each with the same causal rule
+ * as pa_prefill_chunk, and every row's out and lse land at its packed row.
+ * The dispatch guard's choice ("Prefill and decode need different
+ * kernels") is made per work item inside the kernel: each workgroup takes
+ * either a 128-row prefill tile or a whole decode (request, KV head), so a
+ * step needs one launch instead of a prefill launch, a decode launch and a
+ * merge pass, and the MFMA-bound tiles and HBM-bound decode items run on
+ * the chip at the same time.  bf16 only; d = 64 or 128; G in {1, 2, 4, 8};
+ * B <= 512 (PA_ERR_UNSUPPORTED otherwise).  No workspace; prefill tiles are
+ * never split along their keys, so a batch whose prefill is a few very
+ * long chunks is better served by pa_prefill_chunk, which can split.
+ * Requests with n_r <= 0 are skipped. */
+pa_status pa_mixed_attention(const pa_desc* desc, const void* q, const void* k_pool,
+                             const void* v_pool, const int32_t* page_table,
+                             const int32_t* seq_lens, const int32_t* q_offsets,
+                             const int32_t* q_starts, float scale, void* out, float* lse,
+                             void* stream);
+
 /* Append a step's new K and V rows into their page slots (the write that
  * precedes attention in every serving step: the "Paged KV Cache" section of
  * the tiny-llm source reading).  Request r contributes n_r = seq_lens[r] -

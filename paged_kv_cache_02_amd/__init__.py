@@ -57,6 +57,8 @@ _SIGS = {
                                       _P, ctypes.c_size_t, _P, _P, _P]),
     "pa_prefill_chunk": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P,
                                         _P, ctypes.c_size_t, _P]),
+    "pa_mixed_attention": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P,
+                                          _P]),
     "pa_merge_partials": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                          ctypes.c_int32, _P, _P, _P, ctypes.c_int32, _P, _P]),
     "pa_gather_kv": (ctypes.c_int, [_D, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]),
@@ -266,6 +268,30 @@ def pa_prefill_chunk(q, k_pool, v_pool, page_table, seq_lens, q_offsets, scale, 
     return out, lse
 
 
+def pa_mixed_attention(q, k_pool, v_pool, page_table, seq_lens, q_offsets, scale, *,
+                       q_starts=None, max_seq_len=None, max_q_len=None, out=None, lse=None,
+                       desc=None):
+    """One continuous-batching round in one launch: rows with n_r = 1 are
+    decoded, chunks with n_r > 1 prefilled; returns (out, lse)."""
+    desc = desc or make_desc(q, k_pool, page_table, seq_lens, max_seq_len, max_q_len, q_offsets)
+    out, lse = _alloc_out(q, out, lse)
+    _check(lib().pa_mixed_attention(ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                    _ptr(page_table), _ptr(seq_lens), _ptr(q_offsets),
+                                    _ptr(q_starts), float(scale), _ptr(out), _ptr(lse),
+                                    _stream(q.device)),
+           "pa_mixed_attention")
+    return out, lse
+
+
+def bind_mixed_attention(q, k_pool, v_pool, page_table, seq_lens, q_offsets, scale, *, out, lse,
+                         desc, q_starts=None) -> "BoundCall":
+    """pa_mixed_attention with fixed arguments (see BoundCall)."""
+    keep = (desc, q, k_pool, v_pool, page_table, seq_lens, q_offsets, q_starts, out, lse)
+    return BoundCall("pa_mixed_attention", keep, ctypes.byref(desc), _ptr(q), _ptr(k_pool),
+                     _ptr(v_pool), _ptr(page_table), _ptr(seq_lens), _ptr(q_offsets),
+                     _ptr(q_starts), float(scale), _ptr(out), _ptr(lse), _stream(q.device))
+
+
 class BoundCall:
     """One library call with its arguments marshalled once, for launch loops
     in which the per-call Python cost would otherwise starve the GPU queue.
@@ -452,4 +478,4 @@ __all__ = ["pa_desc", "pa_plan_info", "PaError", "lib", "make_desc", "pa_plan",
            "pa_merge_partials", "pa_gather_kv", "pa_validate_metadata", "pa_status_str",
            "split_partials_view", "pa_append_kv", "bind_append_kv", "PagePool", "BoundCall",
            "bind_decode", "bind_prefill_chunk", "pa_copy_pages", "pa_decode_dense",
-           "pa_decode_direct", "EXPORTED"]
+           "pa_decode_direct", "pa_mixed_attention", "bind_mixed_attention", "EXPORTED"]

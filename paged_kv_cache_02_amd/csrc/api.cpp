@@ -464,6 +464,52 @@ pa_status pa_prefill_chunk(const pa_desc* d, const void* q, const void* k_pool,
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+pa_status pa_mixed_attention(const pa_desc* d, const void* q, const void* k_pool,
+                             const void* v_pool, const int32_t* page_table, const int32_t* seq_lens,
+                             const int32_t* q_offsets, const int32_t* q_starts, float scale,
+                             void* out, float* lse, void* stream) {
+  pa_status st = check_desc(d);
+  if (st != PA_OK) return st;
+  if (d->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  if (!pa::decode_group_supported(G)) return PA_ERR_UNSUPPORTED;
+  if (d->num_seqs > pa::kMaxMixedSeqs) return PA_ERR_UNSUPPORTED;
+  if (d->num_seqs == 0 || d->total_q == 0) return PA_OK;
+  if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !q_offsets || !out) return PA_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out) ||
+      !aligned4(page_table) || !aligned4(seq_lens) || !aligned4(q_offsets) ||
+      (q_starts && !aligned4(q_starts)) || (lse && !aligned4(lse)))
+    return PA_ERR_ARG;
+  if (out == q) return PA_ERR_ARG;
+  if (!(scale > 0.f) || !isfinite(scale)) return PA_ERR_ARG;
+  if (d->max_q_len < 1) return PA_ERR_ARG;
+  pa::PrefillArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.page_table = page_table;
+  a.seq_lens = seq_lens;
+  a.q_offsets = q_offsets;
+  a.q_starts = q_starts;
+  a.out = out;
+  a.lse = lse;
+  a.num_seqs = d->num_seqs;
+  a.num_q_heads = d->num_q_heads;
+  a.num_kv_heads = d->num_kv_heads;
+  a.max_pages_per_seq = d->max_pages_per_seq;
+  a.num_pages = d->num_pages;
+  a.tiles_per_seq = 1;
+  a.num_splits = 1;
+  a.kv_tiles_per_split = pa::kMixedUnsplit;
+  a.scale_log2 = scale * kLog2e;
+  const long long items = pa::mixed_items_bound(d->total_q, d->num_seqs, G);
+  const hipError_t e =
+      pa::launch_mixed(a, d->head_dim, G, items, reinterpret_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) return PA_ERR_UNSUPPORTED;
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 pa_status pa_append_kv(const pa_desc* d, const void* k_new, const void* v_new,
                        const int32_t* page_table, const int32_t* seq_lens,
                        const int32_t* q_offsets, const int32_t* q_starts, void* k_pool,

@@ -1,0 +1,518 @@
+// Device building blocks of the paged decode kernels (gfx950): the lane
+// layout of a (page, KV head) block, pipelined K/V block loads, the
+// per-page online-softmax update, and the body that walks one (request, KV
+// head) page range with a workgroup of 4 or 8 waves.  Shared by the decode
+// kernels and the mixed prefill/decode kernel.
+//
+// Lane layout inside a wave, for one (page, KV head) block of 16 keys x d:
+// the block is read as 16-byte chunks; LPT consecutive lanes cover one key
+// row (LPT in {4, 8, 16}, chosen so that the G x d accumulator costs at most
+// 64 floats per lane), so one wave load instruction reads 64/LPT full key
+// rows and every row segment it touches is LPT*16 contiguous bytes.  A
+// lane's score partial for its key is reduced over the LPT lanes of the row
+// with DPP butterflies (quad_perm, row_half_mirror, row_mirror); the softmax
+// state (running max m, running sum l) is per lane and per head, and the
+// lane accumulates p * v for its own dims only.  The running max is updated
+// lazily: the accumulator is rescaled only when a score exceeds the current
+// reference max by more than 2^8, which keeps exp2 bounded and leaves the
+// result exact up to rounding.
+//
+// Scores use v_dot2_f32_bf16 on the stored bf16 pairs (exact products,
+// float32 sums); everything after the dot product is float32.  Scores are
+// kept in base-2 units (scale * log2 e folded in), and lse is converted back
+// to natural log on output.
+//
+// Keys past seq_len in the last page are masked with selects (never a
+// multiply by zero), so NaN in page tails cannot leak; page-table entries
+// past the request's last page are never read.
+#pragma once
+
+#include "pa_internal.h"
+
+#include <math.h>
+
+namespace pa {
+namespace dec {
+
+constexpr float kRescaleLog2 = 8.0f;
+constexpr float kLn2 = 0.693147180559945309f;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+template <typename T, int D, int G>
+struct Shape {
+  static constexpr int kVec = 16 / (int)sizeof(T);   // elements per 16-byte chunk
+  static constexpr int kChunks = D / kVec;            // chunks per key row
+  static constexpr int kAccMax = 32;                  // accumulator floats per lane
+  static constexpr int kLptMin = (G * D + kAccMax - 1) / kAccMax;
+  static constexpr int kLpt0 = kLptMin <= 4 ? 4 : (kLptMin <= 8 ? 8 : 16);
+  static constexpr int kLpt = kLpt0 > kChunks ? kChunks : kLpt0;  // lanes per key row
+  static constexpr int kRowsPerLoad = 64 / kLpt;      // key rows per wave load
+  static constexpr int kKeysPerLane = kPageSize / kRowsPerLoad;
+  static constexpr int kChunksPerLane = kChunks / kLpt;
+  static constexpr int kDimsPerLane = kChunksPerLane * kVec;
+  static_assert(kPageSize % kRowsPerLoad == 0, "page must split into whole wave loads");
+  static_assert(kChunks % kLpt == 0, "row must split into whole lane groups");
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the LPT consecutive lanes that share a key row; every lane of the
+// group receives the total.
+template <int LPT>
+__device__ __forceinline__ float row_group_sum(float x) {
+  x += dpp<0xB1>(x);                              // quad_perm [1,0,3,2]
+  x += dpp<0x4E>(x);                              // quad_perm [2,3,0,1]
+  if constexpr (LPT >= 8) x += dpp<0x141>(x);     // row_half_mirror
+  if constexpr (LPT >= 16) x += dpp<0x140>(x);    // row_mirror
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t u) {
+  return __builtin_bit_cast(bf16x2_t, u);
+}
+
+// Dot product of one 16-byte chunk of q with one 16-byte chunk of k.
+template <typename T>
+__device__ __forceinline__ float chunk_dot(const uint4& q, const uint4& k, float acc);
+
+template <>
+__device__ __forceinline__ float chunk_dot<__bf16>(const uint4& q, const uint4& k, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q.x), as_bf16x2(k.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q.y), as_bf16x2(k.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q.z), as_bf16x2(k.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q.w), as_bf16x2(k.w), acc, false);
+  return acc;
+}
+
+template <>
+__device__ __forceinline__ float chunk_dot<float>(const uint4& q, const uint4& k, float acc) {
+  acc = fmaf(__uint_as_float(q.x), __uint_as_float(k.x), acc);
+  acc = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), acc);
+  acc = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), acc);
+  acc = fmaf(__uint_as_float(q.w), __uint_as_float(k.w), acc);
+  return acc;
+}
+
+// Unpack one 16-byte chunk of V to float32.
+template <typename T>
+__device__ __forceinline__ void chunk_unpack(const uint4& v, float* f);
+
+template <>
+__device__ __forceinline__ void chunk_unpack<__bf16>(const uint4& v, float* f) {
+  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+  f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+
+template <>
+__device__ __forceinline__ void chunk_unpack<float>(const uint4& v, float* f) {
+  f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+  f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+}
+
+template <typename T>
+__device__ __forceinline__ T from_float(float x);
+template <>
+__device__ __forceinline__ __bf16 from_float<__bf16>(float x) { return (__bf16)x; }
+template <>
+__device__ __forceinline__ float from_float<float>(float x) { return x; }
+
+template <typename T, int D, int G>
+struct Half {  // the K (or V) registers of one (page, KV head) block
+  using S = Shape<T, D, G>;
+  uint4 c[S::kKeysPerLane][S::kChunksPerLane];
+};
+
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+// Buffer resource word 3 for gfx9-family raw (unstructured) buffers.
+constexpr int kBufferWord3 = 0x00020000;
+// Cache-policy bits of a buffer load: nontemporal (streamed past the caches).
+constexpr int kLoadNontemporal = 2;
+
+// Issue the loads of one K or V block (16 keys x d, contiguous) through a
+// raw buffer resource that covers exactly that block.  Every K/V byte is read
+// once, so the loads are nontemporal.  A resource with zero records makes
+// every load of the block return zeros without touching memory, which lets
+// the software pipeline issue its lookahead loads unconditionally (the
+// wait counts the compiler inserts then stay exact across iterations).
+template <typename T, int D, int G>
+__device__ __forceinline__ void load_half(Half<T, D, G>& hr, const T* blk, bool live, int row0,
+                                          int col) {
+  using S = Shape<T, D, G>;
+  const int bytes = live ? kPageSize * D * (int)sizeof(T) : 0;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(blk), (short)0, bytes, kBufferWord3);
+#pragma unroll
+  for (int kk = 0; kk < S::kKeysPerLane; ++kk) {
+#pragma unroll
+    for (int jj = 0; jj < S::kChunksPerLane; ++jj) {
+      const int off = (row0 + S::kRowsPerLoad * kk) * D + (col + S::kLpt * jj) * S::kVec;
+      const u32x4_t v =
+          __builtin_amdgcn_raw_buffer_load_b128(rs, off * (int)sizeof(T), 0, kLoadNontemporal);
+      hr.c[kk][jj] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+  }
+}
+
+template <typename T, int D, int G>
+struct WaveState {
+  using S = Shape<T, D, G>;
+  float m[G];
+  float l[G];
+  float acc[G][S::kDimsPerLane];
+};
+
+// Scores of the lane's keys of one page -> probabilities p[kk][h], with the
+// online-softmax reference max and running sum updated.  All scores of the
+// page are formed first and the reference max is moved at most once per
+// page, before any probability is taken, so every p of the page shares the
+// reference the accumulator is kept at.  Keys at index >= live_keys inside
+// the page get p = 0 through selects.
+template <typename T, int D, int G>
+__device__ __forceinline__ void page_scores(const Half<T, D, G>& kr,
+                                            const uint4 (&qv)[G][Shape<T, D, G>::kChunksPerLane],
+                                            WaveState<T, D, G>& st, int live_keys, int row0,
+                                            float scale_log2,
+                                            float (&p)[Shape<T, D, G>::kKeysPerLane][G]) {
+  using S = Shape<T, D, G>;
+  float x[S::kKeysPerLane][G];
+  float xmax[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) xmax[h] = -INFINITY;
+#pragma unroll
+  for (int kk = 0; kk < S::kKeysPerLane; ++kk) {
+    const bool valid = row0 + S::kRowsPerLoad * kk < live_keys;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float s = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < S::kChunksPerLane; ++jj) s = chunk_dot<T>(qv[h][jj], kr.c[kk][jj], s);
+      s = row_group_sum<S::kLpt>(s);
+      x[kk][h] = valid ? s * scale_log2 : -INFINITY;
+      xmax[h] = fmaxf(xmax[h], x[kk][h]);
+    }
+  }
+  bool need = false;
+#pragma unroll
+  for (int h = 0; h < G; ++h) need |= xmax[h] > st.m[h] + kRescaleLog2;
+  if (__builtin_expect(__any(need), 0)) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mn = fmaxf(st.m[h], xmax[h]);
+      const float alpha = (mn == st.m[h]) ? 1.f : fast_exp2(st.m[h] - mn);
+      st.l[h] *= alpha;
+#pragma unroll
+      for (int e = 0; e < S::kDimsPerLane; ++e) st.acc[h][e] *= alpha;
+      st.m[h] = mn;
+    }
+  }
+#pragma unroll
+  for (int kk = 0; kk < S::kKeysPerLane; ++kk) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      // x = -inf (dead key) gives exp2(-inf) = 0; m = -inf only while every
+      // key seen so far is dead, and then x is -inf as well
+      p[kk][h] = x[kk][h] == -INFINITY ? 0.f : fast_exp2(x[kk][h] - st.m[h]);
+      st.l[h] += p[kk][h];
+    }
+  }
+}
+
+// acc += p * V for the lane's keys and dims of one page.
+template <typename T, int D, int G>
+__device__ __forceinline__ void page_values(const Half<T, D, G>& vr, WaveState<T, D, G>& st,
+                                            int live_keys, int row0,
+                                            const float (&p)[Shape<T, D, G>::kKeysPerLane][G]) {
+  using S = Shape<T, D, G>;
+#pragma unroll
+  for (int kk = 0; kk < S::kKeysPerLane; ++kk) {
+    const bool valid = row0 + S::kRowsPerLoad * kk < live_keys;
+#pragma unroll
+    for (int jj = 0; jj < S::kChunksPerLane; ++jj) {
+      uint4 raw = vr.c[kk][jj];
+      // a dead key's V may hold NaN: select it to zero (0 * NaN would leak)
+      raw.x = valid ? raw.x : 0u;
+      raw.y = valid ? raw.y : 0u;
+      raw.z = valid ? raw.z : 0u;
+      raw.w = valid ? raw.w : 0u;
+      float vf[S::kVec];
+      chunk_unpack<T>(raw, vf);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+#pragma unroll
+        for (int e = 0; e < S::kVec; ++e)
+          st.acc[h][jj * S::kVec + e] = fmaf(p[kk][h], vf[e], st.acc[h][jj * S::kVec + e]);
+      }
+    }
+  }
+}
+
+template <typename T, int D, int G>
+__device__ __forceinline__ void reset_state(WaveState<T, D, G>& st) {
+  using S = Shape<T, D, G>;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    st.m[h] = -INFINITY;
+    st.l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < S::kDimsPerLane; ++e) st.acc[h][e] = 0.f;
+  }
+}
+
+// Combine the wave's lanes that hold different keys of the same dims (the
+// lanes that differ in row0): afterwards every lane holds the wave's total
+// m, l and acc for its dims, by the log-sum-exp rule.
+template <typename T, int D, int G>
+__device__ __forceinline__ void wave_combine(WaveState<T, D, G>& st) {
+  using S = Shape<T, D, G>;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float M = st.m[h];
+#pragma unroll
+    for (int o = S::kLpt; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+    const float f = (st.m[h] == -INFINITY) ? 0.f : fast_exp2(st.m[h] - M);
+    float lsum = st.l[h] * f;
+#pragma unroll
+    for (int o = S::kLpt; o < 64; o <<= 1) lsum += __shfl_xor(lsum, o);
+    st.l[h] = lsum;
+    st.m[h] = M;
+#pragma unroll
+    for (int e = 0; e < S::kDimsPerLane; ++e) {
+      float v = st.acc[h][e] * f;
+#pragma unroll
+      for (int o = S::kLpt; o < 64; o <<= 1) v += __shfl_xor(v, o);
+      st.acc[h][e] = v;
+    }
+  }
+}
+
+// q chunks of the lane's dims for the G query heads of KV head g of request
+// r, through a buffer resource; valid = false gives zeros and reads nothing.
+template <typename T, int D, int G>
+using QRegs = uint4[G][Shape<T, D, G>::kChunksPerLane];
+
+template <typename T, int D, int G>
+__device__ __forceinline__ void load_q(QRegs<T, D, G>& qv, const T* q, int Hq, int r, int g,
+                                       bool valid, int col) {
+  using S = Shape<T, D, G>;
+  const T* base = q + ((size_t)r * Hq + (size_t)g * G) * D;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T*>(base), (short)0, valid ? G * D * (int)sizeof(T) : 0, kBufferWord3);
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+#pragma unroll
+    for (int jj = 0; jj < S::kChunksPerLane; ++jj) {
+      const int off = h * D + (col + S::kLpt * jj) * S::kVec;
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, off * (int)sizeof(T), 0, 0);
+      qv[h][jj] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+  }
+}
+
+// Depth of the K/V software pipeline: while page i is scored and accumulated,
+// the K and V blocks of pages i+1 .. i+kDepth are in flight.  The depth is
+// the largest (up to 4) whose buffers still leave room for two waves per
+// SIMD: accumulator + q (+ kExtraRegs) + scores/probabilities + 2 (depth + 1)
+// K/V buffers within 224 VGPRs.
+template <typename T, int D, int G, int kExtraRegs>
+struct Pipe {
+  using S = Shape<T, D, G>;
+  static constexpr int kHalfRegs = (int)(sizeof(Half<T, D, G>) / 4);
+  static constexpr int kFixedRegs = G * S::kDimsPerLane + G * S::kChunksPerLane * 4 +
+                                    2 * G * S::kKeysPerLane + kExtraRegs;
+  static constexpr int kDepth = kFixedRegs + 10 * kHalfRegs <= 224  ? 4
+                                : kFixedRegs + 8 * kHalfRegs <= 224 ? 3
+                                : kFixedRegs + 6 * kHalfRegs <= 224 ? 2
+                                                                    : 1;
+  static constexpr int kBufs = kDepth + 1;
+};
+
+// One (request r, KV head g) over the request's logical pages [pb, pe), the
+// pages dealt round-robin to the workgroup's kW waves (64 * kW threads).
+// Each wave keeps its own online-softmax state; the states are merged
+// through LDS by the log-sum-exp rule (with 8 waves, waves 4..7 first fold
+// into waves 0..3, so the LDS holds four states).  qrow is the request's row
+// of q, out and lse: r itself in a decode batch, the request's packed row in
+// a mixed batch.  Writes out and lse, or the split's normalized partial when
+// a.write_partials.
+//
+// kDense: the same walk over a dense cache [B, Hkv, MP * P, d] (request r's
+// keys of KV head g contiguous, no page table), for measuring what the
+// paging costs; a.max_pages_per_seq is then the cache capacity in pages.
+template <typename T, int D, int G, int kW, bool kDense>
+__device__ __forceinline__ void decode_range(const DecodeArgs& a, int r, int qrow, int g, int split,
+                                             int pb, int pe, int L) {
+  static_assert(kW == 4 || kW == 8, "4 or 8 waves per workgroup");
+  constexpr int kSlots = 4;   // wave states LDS holds at once
+  using S = Shape<T, D, G>;
+  const int32_t num_pages = a.num_pages;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane % S::kLpt;
+  const int row0 = lane / S::kLpt;
+  const int nsplit = a.num_splits;
+  const int Hq = a.num_q_heads;
+  const int Hkv = a.num_kv_heads;
+
+  const T* __restrict__ qp = reinterpret_cast<const T*>(a.q);
+  const T* __restrict__ kpool = reinterpret_cast<const T*>(a.k_pool);
+  const T* __restrict__ vpool = reinterpret_cast<const T*>(a.v_pool);
+  const int32_t* __restrict__ ptab = kDense ? nullptr : a.page_table + (size_t)r * a.max_pages_per_seq;
+
+  // q chunks of the lane's dims for every head of the group
+  uint4 qv[G][S::kChunksPerLane];
+  load_q<T, D, G>(qv, qp, Hq, qrow, g, true, col);
+
+  WaveState<T, D, G> st;
+  reset_state<T, D, G>(st);
+
+  const size_t blk = (size_t)kPageSize * D;  // elements of one (page, head) block
+
+  // The wave's pages are pb + wave + kW * i for i in [0, nw).  The physical
+  // id of the page whose loads are issued next is fetched one step earlier
+  // (a uniform, scalar load), so its latency is hidden behind a page of
+  // work.
+  const int first = pb + wave;
+  const int nw = first < pe ? (pe - first + kW - 1) / kW : 0;
+  auto page_id = [&](int i) -> int {  // clamped index: always a valid entry
+    const int ic = i < nw ? i : nw - 1;
+    if (kDense) return first + kW * ic;
+    int phys = ptab[first + kW * ic];
+    return phys < 0 ? 0 : (phys >= num_pages ? num_pages - 1 : phys);
+  };
+  auto block_ptr = [&](const T* pool, int phys) -> const T* {
+    if (kDense) return pool + (((size_t)r * Hkv + g) * a.max_pages_per_seq + phys) * blk;
+    return pool + ((size_t)phys * Hkv + g) * blk;
+  };
+
+  // Software pipeline Pipe::kDepth pages deep.  K of page i+kDepth is
+  // requested before page i's scores and its V before page i's value update.
+  // The kDepth+1 register buffers rotate through a fully unrolled inner loop,
+  // so no buffer is ever copied.  Lookahead pages past the wave's last one
+  // are loaded with zero-record resources.
+  constexpr int kDepth = Pipe<T, D, G, 0>::kDepth;
+  constexpr int kBufs = Pipe<T, D, G, 0>::kBufs;
+  if (nw > 0) {
+    Half<T, D, G> hk[kBufs], hv[kBufs];
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u) {
+      const int phys = page_id(u);
+      load_half<T, D, G>(hk[u], block_ptr(kpool, phys), u < nw, row0, col);
+      load_half<T, D, G>(hv[u], block_ptr(vpool, phys), u < nw, row0, col);
+    }
+    int next_phys = page_id(kDepth);
+    int i = 0;
+#pragma unroll 1
+    for (;;) {
+#pragma unroll
+      for (int u = 0; u < kBufs; ++u) {
+        const int ahead = i + kDepth;
+        const bool more = ahead < nw;
+        const int nb = (u + kDepth) % kBufs;  // buffer of page i + kDepth
+        const int phys = next_phys;
+        load_half<T, D, G>(hk[nb], block_ptr(kpool, phys), more, row0, col);
+        next_phys = page_id(ahead + 1);
+        const int live = L - (first + kW * i) * kPageSize;  // >= 16 except on the last page
+        float pr[S::kKeysPerLane][G];
+        page_scores<T, D, G>(hk[u], qv, st, live, row0, a.scale_log2, pr);
+        load_half<T, D, G>(hv[nb], block_ptr(vpool, phys), more, row0, col);
+        page_values<T, D, G>(hv[u], st, live, row0, pr);
+        if (++i >= nw) goto pages_done;
+      }
+    }
+  }
+pages_done:
+
+  wave_combine<T, D, G>(st);
+
+  // ---- merge the waves through LDS ----
+  __shared__ float sm_m[kSlots][G];
+  __shared__ float sm_l[kSlots][G];
+  __shared__ float sm_acc[kSlots][G][D];
+  auto put = [&](int slot) {
+    if (row0 == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        if (col == 0) {
+          sm_m[slot][h] = st.m[h];
+          sm_l[slot][h] = st.l[h];
+        }
+#pragma unroll
+        for (int jj = 0; jj < S::kChunksPerLane; ++jj)
+#pragma unroll
+          for (int e = 0; e < S::kVec; ++e)
+            sm_acc[slot][h][(col + S::kLpt * jj) * S::kVec + e] = st.acc[h][jj * S::kVec + e];
+      }
+    }
+  };
+  if constexpr (kW > kSlots) {
+    // waves kSlots.. hand their states to waves 0..kSlots-1, lane by lane
+    if (wave >= kSlots) put(wave - kSlots);
+    __syncthreads();
+    if (wave < kSlots && row0 == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float mb = sm_m[wave][h];
+        const float lb = sm_l[wave][h];
+        const float M = fmaxf(st.m[h], mb);
+        const float fa = (st.m[h] == -INFINITY) ? 0.f : fast_exp2(st.m[h] - M);
+        const float fb = (mb == -INFINITY) ? 0.f : fast_exp2(mb - M);
+#pragma unroll
+        for (int jj = 0; jj < S::kChunksPerLane; ++jj)
+#pragma unroll
+          for (int e = 0; e < S::kVec; ++e) {
+            const float vb = sm_acc[wave][h][(col + S::kLpt * jj) * S::kVec + e];
+            st.acc[h][jj * S::kVec + e] = st.acc[h][jj * S::kVec + e] * fa + vb * fb;
+          }
+        st.l[h] = st.l[h] * fa + lb * fb;
+        st.m[h] = M;
+      }
+    }
+    __syncthreads();
+  }
+  if (wave < kSlots) put(wave);
+  __syncthreads();
+
+  for (int idx = threadIdx.x; idx < G * D; idx += 64 * kW) {
+    const int h = idx / D;
+    const int dim = idx % D;
+    float Mt = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kSlots; ++w) Mt = fmaxf(Mt, sm_m[w][h]);
+    float lt = 0.f, ot = 0.f;
+#pragma unroll
+    for (int w = 0; w < kSlots; ++w) {
+      const float mw = sm_m[w][h];
+      const float f = (mw == -INFINITY) ? 0.f : fast_exp2(mw - Mt);
+      lt += f * sm_l[w][h];
+      ot += f * sm_acc[w][h][dim];
+    }
+    const int hq = g * G + h;
+    const bool empty = !(lt > 0.f);
+    const float o = empty ? 0.f : ot / lt;
+    const float lse2 = empty ? -INFINITY : (Mt + __log2f(lt)) * kLn2;
+    if (!a.write_partials) {
+      T* out = reinterpret_cast<T*>(a.out);
+      out[((size_t)qrow * Hq + hq) * D + dim] = from_float<T>(o);
+      if (a.lse != nullptr && dim == 0) a.lse[(size_t)qrow * Hq + hq] = lse2;
+    } else {
+      const size_t row = ((size_t)qrow * Hq + hq) * nsplit + split;
+      a.o_part[row * D + dim] = o;
+      if (dim == 0) a.lse_part[row] = lse2;
+    }
+  }
+}
+
+}  // namespace dec
+}  // namespace pa

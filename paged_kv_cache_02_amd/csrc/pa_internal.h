@@ -14,6 +14,11 @@ constexpr int kPageSize = 16;  // keys per page (the only page size built)
 // Requests the page-balanced decode handles in one call (its per-request page
 // prefix lives in LDS).
 constexpr int kMaxBalancedSeqs = 4096;
+// Requests the mixed prefill/decode kernel handles in one call (each
+// workgroup ranks them in LDS).
+constexpr int kMaxMixedSeqs = 512;
+// KV tiles per split that leaves every prefill row tile whole.
+constexpr int kMixedUnsplit = 1 << 29;
 
 // ---------------------------------------------------------------------------
 // decode / split-K partition kernel
@@ -109,6 +114,19 @@ struct PrefillArgs {
 int prefill_tile_rows(int head_dim);
 int prefill_tile_keys();
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int group, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// mixed prefill/decode batch in one launch (bf16; group in {1, 2, 4, 8})
+// ---------------------------------------------------------------------------
+// Upper bound on the work items of one KV head (prefill row tiles plus
+// decode requests) of a batch with total_q query rows over num_seqs
+// requests; the grid is this times Hkv, and surplus workgroups exit.
+long long mixed_items_bound(long long total_q, int num_seqs, int group);
+// Tiles are never split: the caller sets a.num_splits = 1 and
+// a.kv_tiles_per_split = kMixedUnsplit; a.tiles_per_seq, a.part_o and
+// a.part_lse are not used.
+hipError_t launch_mixed(const PrefillArgs& a, int head_dim, int group, long long items_per_head,
+                        hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // KV append (new rows into their page slots)

@@ -144,3 +144,23 @@ def test_empty_batches_are_no_ops():
     rc = L.pa_decode(ctypes.byref(d), None, None, None, None, None, None, 0.1, None, None, None, 0,
                      None)
     assert rc == pa.PA_OK
+
+
+def test_mixed_attention_host_checks():
+    L = pa.lib()
+    d = desc(B=64, total_q=2108, max_q_len=512, max_seq_len=4096)
+    # null pointers are rejected before any launch
+    rc = L.pa_mixed_attention(ctypes.byref(d), None, None, None, None, None, None, None, 0.1, None,
+                              None, None)
+    assert rc == pa.PA_ERR_ARG
+    # bf16 only, G in {1, 2, 4, 8}, at most 512 requests
+    for bad in (desc(B=64, total_q=64, dtype=pa.PA_F32), desc(B=64, Hq=24, Hkv=8, total_q=64),
+                desc(B=513, total_q=513), desc(B=64, Hq=16, Hkv=1, total_q=64)):
+        rc = L.pa_mixed_attention(ctypes.byref(bad), None, None, None, None, None, None, None, 0.1,
+                                  None, None, None)
+        assert rc == pa.PA_ERR_UNSUPPORTED
+    # an empty batch is a no-op
+    e = desc(B=0, total_q=0)
+    rc = L.pa_mixed_attention(ctypes.byref(e), None, None, None, None, None, None, None, 0.1, None,
+                              None, None)
+    assert rc == pa.PA_OK
