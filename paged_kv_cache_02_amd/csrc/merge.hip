@@ -9,7 +9,8 @@
 //
 // One wave per (row, head): lanes read the S partial lse values (strided by
 // 64), reduce max and sum with wave shuffles, then each lane produces d/64 of
-// the output dims, reading the S partial rows coalesced.  Partials come
+// the output dims, reading the S partial rows coalesced, eight partials per
+// batch of loads.  Partials come
 // either S per (row, head) (equal splits) or as a variable run of slots per
 // row given by a range table (page-balanced splits).
 #include "pa_internal.h"
@@ -79,16 +80,30 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) merge_kernel(MergeArgs a)
   const float LSE = empty ? -INFINITY : Mb + logf(tot);
 
   constexpr int kPer = D / 64;
+  constexpr int kBatch = 8;   // partial rows requested together
   float acc[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) acc[i] = 0.f;
   if (!empty) {
-    for (int s = 0; s < S; ++s) {
-      const long long row = base + s * step;
-      const float v = lp[row];
-      const float w = (v == -INFINITY) ? 0.f : exp2f((v - LSE) * kLog2e);
+    // the rows of kBatch partials (and their lse) are requested before any
+    // is used, so the loop waits for one memory round trip per batch
+    for (int s0 = 0; s0 < S; s0 += kBatch) {
+      float v[kBatch];
+      float o[kBatch][kPer];
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) acc[i] = fmaf(w, op[row * D + lane + 64 * i], acc[i]);
+      for (int j = 0; j < kBatch; ++j) {
+        const bool live = s0 + j < S;
+        const long long row = base + (long long)(live ? s0 + j : s0) * step;
+        v[j] = live ? lp[row] : -INFINITY;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) o[j][i] = live ? op[row * D + lane + 64 * i] : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const float w = (v[j] == -INFINITY) ? 0.f : exp2f((v[j] - LSE) * kLog2e);
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) acc[i] = fmaf(w, o[j][i], acc[i]);
+      }
     }
   }
   T* out = reinterpret_cast<T*>(a.out) + rh * D;

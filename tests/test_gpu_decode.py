@@ -318,6 +318,43 @@ def test_balanced_one_long_request():
     compare(b, out, lse, ro, rl, label="balanced, one 20000-key request")
 
 
+def test_balanced_workspace_reuse_and_leftover_contents():
+    # the balanced route's workspace holds partials and a range table: a
+    # second call on it, a call after another batch used it, and a call on
+    # a workspace full of random bytes all give the same bits
+    rng = np.random.default_rng(65)
+    b = ragged(65, rng.integers(1, 3000, size=48), 32, 8, 128)
+    other = ragged(66, rng.integers(1, 500, size=300), 32, 8, 128)
+    dev, dev_o = device_batch(b), device_batch(other)
+    desc = pa.make_desc(dev["q"], dev["k_pool"], dev["page_table"], dev["seq_lens"], b.max_seq_len)
+    desc_o = pa.make_desc(dev_o["q"], dev_o["k_pool"], dev_o["page_table"], dev_o["seq_lens"],
+                          other.max_seq_len)
+    assert pa.pa_plan(desc)["path"] == "decode_balanced"
+    need = max(pa.pa_plan(desc)["workspace_bytes"], pa.pa_plan(desc_o)["workspace_bytes"])
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+
+    def call(d, dv, bb):
+        out, lse = pa.pa_decode(dv["q"], dv["k_pool"], dv["v_pool"], dv["page_table"], dv["seq_lens"],
+                                dv["q_offsets"], bb.scale, workspace=ws, desc=d)
+        torch.cuda.synchronize()
+        return out, lse
+
+    print("case balanced workspace reuse", flush=True)
+    out1, lse1 = call(desc, dev, b)
+    out2, lse2 = call(desc, dev, b)
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+    out_o, lse_o = call(desc_o, dev_o, other)
+    out3, lse3 = call(desc, dev, b)
+    assert torch.equal(out1, out3) and torch.equal(lse1, lse3)
+    ws.copy_(torch.randint(0, 256, (need,), dtype=torch.uint8, device="cuda"))
+    out4, lse4 = call(desc, dev, b)
+    assert torch.equal(out1, out4) and torch.equal(lse1, lse4)
+    ro, rl = oracle_run(b)
+    compare(b, out1, lse1, ro, rl, label="balanced, reused workspace")
+    ro, rl = oracle_run(other)
+    compare(other, out_o, lse_o, ro, rl, label="balanced, other batch on the same workspace")
+
+
 @pytest.mark.parametrize("Hq,Hkv,d,dtype", [(8, 8, 128, W.BF16), (16, 8, 128, W.BF16),
                                             (32, 8, 64, W.BF16), (64, 8, 128, W.BF16),
                                             (64, 8, 64, W.BF16), (64, 64, 128, W.BF16),
