@@ -50,13 +50,15 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0,
                     help="wall-clock budget of the oracle's CPU baseline sample")
-    ap.add_argument("--mode", choices=("step", "copy", "baselines"), default="step",
+    ap.add_argument("--mode", choices=("step", "copy", "baselines", "configs"), default="step",
                     help="step: the benchmark; copy: calibration of the HBM counters and "
                          "the streaming ceiling (a plain 1 GiB device copy and a read-only "
                          "reduction of known size); baselines: the Qwen3-4B-shaped decode "
                          "through the production route, the same fused kernel unsplit over "
                          "pages and over a dense cache, and direct (non-flash) paged "
-                         "attention")
+                         "attention; configs: one JSON line per named config and route "
+                         "(cache-flushed per-call times, rate against peak, error against "
+                         "the oracle on sampled requests)")
     return ap.parse_args()
 
 
@@ -157,6 +159,109 @@ def baselines(steps: int, warmup: int):
     print(json.dumps({"baselines": res, "workload": "qwen3_4b_decode", "alg_bytes": nbytes}), flush=True)
 
 
+def config_sweep(iters: int, warmup: int):
+    """One JSON line per named config and route.  Every call is timed on its
+    own with HIP events after a 512 MiB write that leaves neither the 256 MB
+    last-level cache nor the L2s holding any input; median, p10 and p90 over
+    `iters` calls.  The inputs are the parity inputs (page tails and unused
+    pages NaN), and the line carries the largest error against the oracle on
+    a sample of requests with the oracle's own time on that sample."""
+    import torch
+    import oracle as ORACLE
+    import paged_kv_cache_02_amd as pa
+    import workloads as W
+    dev = torch.device("cuda:0")
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+
+    def to_dev(arr, dtype):
+        t = (torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+             if dtype == W.BF16 else torch.from_numpy(np.ascontiguousarray(arr)))
+        return t.to(dev)
+
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+    rng = np.random.default_rng(11)
+    for name in ("tiny_decode", "qwen3_0p6b_decode", "qwen3_4b_decode", "mixed_step",
+                 "long_splitk_decode"):
+        full = W.make_config(name)
+        if name == "mixed_step":
+            routes = [("prefill", full.subset(*full.notes["prefill_requests"], name="chunks")),
+                      ("decode", full.subset(*full.notes["decode_requests"], name="decode rows"))]
+        elif name == "long_splitk_decode":
+            routes = [("decode", full), ("split_merge_S16", full)]
+        else:
+            routes = [("decode", full)]
+        kp, vp = to_dev(full.k_pool, full.dtype), to_dev(full.v_pool, full.dtype)
+        for route, b in routes:
+            q = to_dev(b.q, b.dtype)
+            pt, sl, qo, qs = i32(b.page_table), i32(b.seq_lens), i32(b.q_offsets), i32(b.q_row_starts)
+            desc = pa.make_desc(q, kp, pt, sl, b.max_seq_len, b.max_q_len)
+            out = torch.empty_like(q)
+            lse = torch.empty(b.total_q, b.num_q_heads, dtype=torch.float32, device=dev)
+            if route == "prefill":
+                need = pa.pa_plan(desc)["workspace_bytes"]
+                ws = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+                fn = pa.bind_prefill_chunk(q, kp, vp, pt, sl, qo, b.scale, q_starts=qs, out=out,
+                                           lse=lse, workspace=ws, desc=desc)
+            elif route == "decode":
+                ws = torch.empty(max(pa.pa_plan(desc)["workspace_bytes"], 256), dtype=torch.uint8,
+                                 device=dev)
+                fn = pa.bind_decode(q, kp, vp, pt, sl, qo, b.scale, out=out, lse=lse, workspace=ws,
+                                    desc=desc)
+            else:
+                ws = torch.empty(pa.pa_workspace_bytes(desc, 16), dtype=torch.uint8, device=dev)
+                fn = lambda: pa.pa_split_merge(q, kp, vp, pt, sl, qo, b.scale, 16, out=out, lse=lse,
+                                               workspace=ws, desc=desc)
+            times = []
+            for i in range(warmup + iters):
+                flush.fill_(i & 255)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                if i >= warmup:
+                    times.append((e0, e1))
+            torch.cuda.synchronize()
+            us = np.array([a.elapsed_time(z) * 1e3 for a, z in times])
+            t50, t10, t90 = (float(np.percentile(us, p)) for p in (50, 10, 90))
+            if route == "prefill":
+                work, unit, peak = prefill_alg_flops(b), "TFLOP/s", MFMA_BF16_PEAK_TFLOPS
+                rate = work / (t50 * 1e-6) / 1e12
+            else:
+                work, unit, peak = decode_alg_bytes(b), "GB/s", HBM_PEAK_GBS
+                rate = work / (t50 * 1e-6) / 1e9
+            # parity on a sample of requests (their rows), with the oracle timed
+            nsamp = min(b.num_seqs, 2 if route == "prefill" else 6)
+            pick = (np.arange(nsamp) if route == "prefill"
+                    else np.sort(rng.choice(b.num_seqs, nsamp, replace=False)))
+            t0 = time.perf_counter()
+            ro, rl = ORACLE.paged_attention(b.q_f32(), b.k_pool_f32(), b.v_pool_f32(), b.page_table,
+                                            b.seq_lens, b.q_offsets, b.scale, requests=pick)
+            oracle_s = time.perf_counter() - t0
+            rows = np.concatenate([np.arange(b.q_row_starts[r], b.q_row_starts[r] + b.q_lens[r])
+                                   for r in pick])
+            o = out.float().cpu().numpy().astype(np.float64)[rows]
+            l = lse.cpu().numpy().astype(np.float64)[rows]
+            line = {
+                "config": name, "route": route, "seed": int(full.seed),
+                "shapes": {"B": int(b.num_seqs), "Hq": int(b.num_q_heads), "Hkv": int(b.num_kv_heads),
+                           "d": int(b.head_dim), "page": int(b.page_size), "dtype": b.dtype,
+                           "rows": int(b.total_q), "pool_pages": int(full.num_pages)},
+                "sum_L": int(b.seq_lens.astype(np.int64).sum()),
+                "work": int(work), "work_unit": "FLOP" if route == "prefill" else "B",
+                "t_median_us": round(t50, 2), "t_p10_us": round(t10, 2), "t_p90_us": round(t90, 2),
+                "rate": round(rate, 2), "rate_unit": unit, "frac_of_peak": round(rate / peak, 4),
+                "max_abs_out_err": float(np.max(np.abs(o - ro[rows]))),
+                "max_abs_lse_err": float(np.max(np.abs(l - rl[rows]))),
+                "sample": f"{len(pick)} of {b.num_seqs} requests ({len(rows)} rows)",
+                "oracle_s": round(oracle_s, 3), "host_cores": int(cores),
+            }
+            print(json.dumps(line), flush=True)
+            del q, out, lse, ws
+        del kp, vp
+        torch.cuda.empty_cache()
+
+
 def source_hash(*names) -> str:
     h = hashlib.sha256()
     for n in names:
@@ -168,7 +273,7 @@ def source_hash(*names) -> str:
 def decode_alg_bytes(b) -> int:
     """K and V of every visible key once per KV head, q, out, lse, the page
     table entries read and the two int32 metadata arrays."""
-    es = 2
+    es = 4 if b.dtype == "f32" else 2
     keys = int(b.seq_lens.astype(np.int64).sum())
     pages = int(((b.seq_lens.astype(np.int64) + b.page_size - 1) // b.page_size).sum())
     B, Hq, d = b.num_seqs, b.num_q_heads, b.head_dim
@@ -269,6 +374,9 @@ def main():
         return
     if args.mode == "baselines":
         baselines(args.steps, args.warmup)
+        return
+    if args.mode == "configs":
+        config_sweep(args.steps, args.warmup)
         return
     torch.cuda.init()
     dev = torch.device("cuda:0")
