@@ -209,29 +209,38 @@ __device__ __forceinline__ void dma_tile(unsigned char* kst, unsigned char* vst,
   const int key_base = kt * kTileKeys + wave * kPageSize;   // absolute key of the page's slot 0
   const size_t page_off = ((size_t)(id < 0 ? 0 : id) * Hkv + g) * ((size_t)kPageSize * D);
   const bool full = id >= 0 && key_base + kPageSize <= L;
-#pragma unroll
-  for (int i = 0; i < kPerWave; ++i) {
-    const int u = wave * kPerWave + i;                     // 1 KB piece of the tile
-    // K: key rows in order, 16-byte chunks XOR-swizzled by key
-    const int kslot = i * GE::kKeysPerDma + lane / GE::kRowChunks;   // key within the page
-    const int kchunk = (lane % GE::kRowChunks) ^ swz<D>(wave * kPageSize + kslot);
-    const size_t koff = page_off + (size_t)kslot * D + kchunk * 8;
-    // V: the piece's keys as [dim block][key][4 chunks], so the transposing
-    // reads of one dim block touch kKeysPerDma x 64 consecutive bytes
-    const int vslot = i * GE::kKeysPerDma + (lane / 4) % GE::kKeysPerDma;
+  // lane offsets of piece i: K rows in order with their 16-byte chunks
+  // XOR-swizzled by key; V as [dim block][key][4 chunks], so the transposing
+  // reads of one dim block touch kKeysPerDma x 64 consecutive bytes
+  auto kslot = [&](int i) { return i * GE::kKeysPerDma + lane / GE::kRowChunks; };
+  auto vslot = [&](int i) { return i * GE::kKeysPerDma + (lane / 4) % GE::kKeysPerDma; };
+  auto koff = [&](int i) {
+    const int kchunk = (lane % GE::kRowChunks) ^ swz<D>(wave * kPageSize + kslot(i));
+    return page_off + (size_t)kslot(i) * D + kchunk * 8;
+  };
+  auto voff = [&](int i) {
     const int vchunk = 4 * (lane / (4 * GE::kKeysPerDma)) + (lane & 3);
-    const size_t voff = page_off + (size_t)vslot * D + vchunk * 8;
-    unsigned char* kdst = kst + u * 1024;
-    unsigned char* vdst = vst + u * 1024;
-    if (full) {
-      __builtin_amdgcn_global_load_lds(kpool + koff, (lds_void*)kdst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vpool + voff, (lds_void*)vdst, 16, 0, 0);
-    } else {
+    return page_off + (size_t)vslot(i) * D + vchunk * 8;
+  };
+  if (full) {
+    // the common case, decided once per page: kPerWave DMA instructions for
+    // K and as many for V, back to back
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i)
+      __builtin_amdgcn_global_load_lds(kpool + koff(i), (lds_void*)(kst + (wave * kPerWave + i) * 1024),
+                                       16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i)
+      __builtin_amdgcn_global_load_lds(vpool + voff(i), (lds_void*)(vst + (wave * kPerWave + i) * 1024),
+                                       16, 0, 0);
+  } else {
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
       uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-      if (id >= 0 && key_base + kslot < L) kv = *reinterpret_cast<const uint4*>(kpool + koff);
-      if (id >= 0 && key_base + vslot < L) vv = *reinterpret_cast<const uint4*>(vpool + voff);
-      *reinterpret_cast<uint4*>(kdst + lane * 16) = kv;
-      *reinterpret_cast<uint4*>(vdst + lane * 16) = vv;
+      if (id >= 0 && key_base + kslot(i) < L) kv = *reinterpret_cast<const uint4*>(kpool + koff(i));
+      if (id >= 0 && key_base + vslot(i) < L) vv = *reinterpret_cast<const uint4*>(vpool + voff(i));
+      *reinterpret_cast<uint4*>(kst + (wave * kPerWave + i) * 1024 + lane * 16) = kv;
+      *reinterpret_cast<uint4*>(vst + (wave * kPerWave + i) * 1024 + lane * 16) = vv;
     }
   }
 }
