@@ -531,7 +531,7 @@ def main():
         "decode": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
                    "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                    "traffic": load_traffic("decode", dc_hash), "ms": round(dc_ms, 4),
-                   "kernel": ("decode_balanced_kernel<bf16,128,4> + merge_kernel"
+                   "kernel": ("decode_mfma_kernel<128,4> + merge_kernel"
                               if dc_plan["path"] == "decode_balanced" else
                               f"decode_kernel<bf16,128,4> x{dc_plan['num_splits']} + merge_kernel"),
                    "work": dec_bytes, "work_unit": "B"},

@@ -1,5 +1,10 @@
 // Paged decode attention and its split-K partitions (gfx950).
 //
+// Kernels: decode_kernel (one workgroup per (request, KV head, split), VALU,
+// bf16 and fp32), decode_balanced_kernel (the page-balanced split, VALU:
+// fp32), and decode_mfma_kernel (the page-balanced split with both
+// contractions on MFMA: bf16).
+//
 // One workgroup owns one (request, KV head, split) triple, so the G query
 // heads of a GQA group share every K/V page load (GQA: week-1 material of the
 // tiny-llm source reading; one kernel that walks the page table and runs
@@ -294,6 +299,388 @@ decode_balanced_kernel(DecodeArgs a, const int32_t* __restrict__ page_table,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Page-balanced decode with both contractions on MFMA (bf16).
+//
+// Same ranges, partial slots and merge as decode_balanced_kernel; only the
+// work per (page, KV head) block differs.  With the VALU form above, the
+// dot products, their DPP reductions and the p * V FMAs (about 350 VALU
+// instructions per page and wave) hold the memory stream back; here one
+// page costs D/32 + 2 D/16 MFMAs and a few dozen VALU instructions:
+//   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16: A = the page's 16 keys (lane
+//     j holds key j%16, dims 32c + 8(j/16) .. +7 of k-step c: one 16-byte
+//     load each), B = Q^T with the G query heads in columns 0..G-1 (the other
+//     columns read zeros);
+//   * the result holds, in lane j, keys 4(j/16) .. +3 of head j%16, which is
+//     the A operand layout of O += P V with v_mfma_f32_16x16x16bf16_1k, so
+//     the probabilities go from the softmax straight into the MFMA (as a
+//     bf16 high part and a bf16 remainder, two MFMAs, so that the products
+//     keep about 16 bits);
+//   * V's B operand (4 consecutive keys of one dim per lane) comes from the
+//     wave's own LDS slot through ds_read_b64_tr_b16: the wave writes its V
+//     block there (16-byte chunks XOR-swizzled by key, so both the writes
+//     and the transposing reads are free of bank conflicts) and reads it
+//     back in the same order, so no barrier is needed;
+//   * online softmax per head over the page's 16 keys: the running max is
+//     kept per head (replicated in the head's four lanes), the running sum
+//     per lane and folded at the request's end.
+// Rows 0..G-1 of the 16-row MFMA tiles carry the G query heads; the others
+// are padding whose results are never written.
+// ---------------------------------------------------------------------------
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef short shortx4_t __attribute__((ext_vector_type(4)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+template <int D>
+struct MShape {
+  static constexpr int kKSteps = D / 32;                // 16x16x32 steps of S^T
+  static constexpr int kDimBlocks = D / 16;             // 16-dim output blocks of O
+  static constexpr int kRowBytes = D * 2;               // one key row (bf16)
+  static constexpr int kChunks = D / 8;                 // 16-byte chunks per key row
+  static constexpr int kVLoads = kPageSize * D * 2 / 1024;   // 1 KB wave loads per V block
+  static constexpr int kKeysPerVLoad = 1024 / kRowBytes;
+};
+
+// XOR swizzle of a key row's 16-byte chunks in the LDS slot (bit 0 left
+// alone: the two chunks of one 16-dim block differ in it).
+template <int D>
+__device__ __forceinline__ int vswz(int key) {
+  return D == 128 ? ((key & 7) << 1) : (((key >> 1) & 3) << 1);
+}
+
+template <int D>
+struct MBlock {  // one (page, KV head) block in registers: K as the S^T A operand, V as loaded
+  uint4 k[MShape<D>::kKSteps];
+  uint4 v[MShape<D>::kVLoads];
+};
+
+template <int D>
+__device__ __forceinline__ void load_mblock(MBlock<D>& b, const __bf16* kblk, const __bf16* vblk, bool live,
+                                            int lane) {
+  using M = MShape<D>;
+  const int bytes = live ? kPageSize * M::kRowBytes : 0;
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(kblk), (short)0, bytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(vblk), (short)0, bytes, kBufferWord3);
+#pragma unroll
+  for (int c = 0; c < M::kKSteps; ++c) {
+    const int off = (lane & 15) * M::kRowBytes + (32 * c + 8 * (lane >> 4)) * 2;
+    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, kLoadNontemporal);
+    b.k[c] = make_uint4(x[0], x[1], x[2], x[3]);
+  }
+#pragma unroll
+  for (int t = 0; t < M::kVLoads; ++t) {
+    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rv, t * 1024 + lane * 16, 0, kLoadNontemporal);
+    b.v[t] = make_uint4(x[0], x[1], x[2], x[3]);
+  }
+}
+
+template <int D>
+struct MState {
+  floatx4_t o[MShape<D>::kDimBlocks];   // lane j, reg i: head 4(j/16)+i, dim 16b + j%16
+  float m;                              // running max of head j%16 (log2 units)
+  float l;                              // this lane's part of head j%16's running sum
+};
+
+template <int D>
+__device__ __forceinline__ void mreset(MState<D>& st) {
+#pragma unroll
+  for (int b = 0; b < MShape<D>::kDimBlocks; ++b) st.o[b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  st.m = -INFINITY;
+  st.l = 0.f;
+}
+
+// Q^T for one (row, KV head): lane j holds head j%16's dims 32c + 8(j/16)
+// .. +7; heads at or past G read zeros (the resource covers G heads).
+template <int D, int G>
+__device__ __forceinline__ void load_qt(uint4 (&qt)[MShape<D>::kKSteps], const __bf16* q, int Hq, int row,
+                                        int g, bool valid, int lane) {
+  using M = MShape<D>;
+  const __bf16* base = q + ((size_t)row * Hq + (size_t)g * G) * D;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<__bf16*>(base), (short)0, valid ? G * M::kRowBytes : 0, kBufferWord3);
+#pragma unroll
+  for (int c = 0; c < M::kKSteps; ++c) {
+    const int off = (lane & 15) * M::kRowBytes + (32 * c + 8 * (lane >> 4)) * 2;
+    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+    qt[c] = make_uint4(x[0], x[1], x[2], x[3]);
+  }
+}
+
+template <int D, int G>
+__device__ __forceinline__ void page_mfma(const MBlock<D>& b, const uint4 (&qt)[MShape<D>::kKSteps],
+                                          MState<D>& st, int live, float scale_log2,
+                                          unsigned char* vslot, int lane) {
+  using M = MShape<D>;
+  const int qg = lane >> 4;
+  const int h = lane & 15;
+  // ---- S^T = K Q^T
+  floatx4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < M::kKSteps; ++c)
+    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b.k[c]),
+                                                __builtin_bit_cast(bf16x8_t, qt[c]), s, 0, 0, 0);
+  // ---- V into the wave's LDS slot; keys at or past `live` (possibly NaN)
+  // become zeros
+#pragma unroll
+  for (int t = 0; t < M::kVLoads; ++t) {
+    const int key = t * M::kKeysPerVLoad + lane / M::kChunks;
+    const int chunk = lane % M::kChunks;
+    uint4 x = b.v[t];
+    const bool ok = key < live;
+    x.x = ok ? x.x : 0u;
+    x.y = ok ? x.y : 0u;
+    x.z = ok ? x.z : 0u;
+    x.w = ok ? x.w : 0u;
+    *reinterpret_cast<uint4*>(vslot + key * M::kRowBytes + ((chunk ^ vswz<D>(key)) << 4)) = x;
+  }
+  // ---- online softmax of head h over keys 4qg .. 4qg + 3 of the page
+  float x[4];
+  float xm = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = (4 * qg + i < live && h < G) ? s[i] * scale_log2 : -INFINITY;
+    xm = fmaxf(xm, x[i]);
+  }
+  xm = fmaxf(xm, __shfl_xor(xm, 16));
+  xm = fmaxf(xm, __shfl_xor(xm, 32));
+  if (__builtin_expect(__any(xm > st.m + kRescaleLog2), 0)) {
+    const float mn = fmaxf(st.m, xm);
+    const float alpha = (mn == st.m) ? 1.f : fast_exp2(st.m - mn);
+    st.l *= alpha;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float ai = __shfl(alpha, 4 * qg + i);   // output row 4qg + i is head 4qg + i
+#pragma unroll
+      for (int bb = 0; bb < M::kDimBlocks; ++bb) st.o[bb][i] *= ai;
+    }
+    st.m = mn;
+  }
+  const float mref = st.m == -INFINITY ? 0.f : st.m;
+  float p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    p[i] = x[i] == -INFINITY ? 0.f : fast_exp2(x[i] - mref);
+    st.l += p[i];
+  }
+  // p as the sum of two bf16 parts: a single bf16 rounding (2^-9 relative)
+  // would move outputs of a few keys by up to |v| * 2^-9, which with
+  // |v| ~ 4 is a bf16 output step; with hi + lo the products keep about 16
+  // bits, and V itself is exact
+  bf16x4_t pa, pb;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    pa[i] = (__bf16)p[i];
+    pb[i] = (__bf16)(p[i] - (float)pa[i]);
+  }
+  // ---- O += P V: V's B operand through the transposing LDS read (key
+  // 4qg + h/4, dims 16bb + 4(h%4) .. +3 in this lane's address)
+  const int vkey = 4 * qg + (h >> 2);
+#pragma unroll
+  for (int bb = 0; bb < M::kDimBlocks; ++bb) {
+    const int dim = 16 * bb + 4 * (h & 3);
+    const unsigned char* pa_addr =
+        vslot + vkey * M::kRowBytes + (((dim >> 3) ^ vswz<D>(vkey)) << 4) + (dim & 7) * 2;
+    const shortx4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) shortx4_t*)(pa_addr));
+    const bf16x4_t vb = __builtin_bit_cast(bf16x4_t, r);
+    st.o[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, st.o[bb], 0, 0, 0);
+    st.o[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pb, vb, st.o[bb], 0, 0, 0);
+  }
+}
+
+// Head totals at a request's end: l summed over the head's four lanes.
+template <int D>
+__device__ __forceinline__ float head_sum(const MState<D>& st) {
+  float l = st.l;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  return l;
+}
+
+template <int D, int G>
+__global__ void __launch_bounds__(kThreads, 2)
+decode_mfma_kernel(DecodeArgs a, const int32_t* __restrict__ page_table,
+                   const int32_t* __restrict__ seq_lens, float* __restrict__ o_part,
+                   float* __restrict__ lse_part, int32_t* __restrict__ range_meta) {
+  using M = MShape<D>;
+  static_assert(G <= 16, "at most 16 query heads per KV head");
+  constexpr int kDepth = 3;
+  constexpr int kBufs = kDepth + 1;
+  __shared__ int pre[kMaxBalancedSeqs + 1];
+  __shared__ __align__(16) unsigned char vslots[kWaves][kPageSize * M::kRowBytes];
+
+  const int32_t num_pages = a.num_pages;
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int Hq = a.num_q_heads;
+  const int Hkv = a.num_kv_heads;
+  const int B = a.num_seqs;
+  const int maxp = a.max_pages_per_seq;
+  const int V = a.num_splits;
+  const int g = blockIdx.x % Hkv;
+  const int v = (blockIdx.x / Hkv) * kWaves + wave;
+  unsigned char* vslot = vslots[wave];
+
+  page_prefix(pre, seq_lens, B, maxp);
+  const int N = uniform(pre[B]);
+  const int per = N > 0 ? (N + V - 1) / V : 1;  // pages per wave range
+
+  if (blockIdx.x == 0) {
+    for (int r = threadIdx.x; r < B; r += kThreads) {
+      const int s0 = pre[r], s1 = pre[r + 1];
+      range_meta[2 * r] = s0 < s1 ? s0 / per : 0;
+      range_meta[2 * r + 1] = s0 < s1 ? (s1 - 1) / per : -1;
+    }
+  }
+
+  const long long f0l = (long long)v * per;
+  if (f0l >= N) return;
+  const int f0 = (int)f0l;
+  const int nw = (f0 + per < N ? f0 + per : N) - f0;
+
+  auto npages = [&](int r) -> int { return uniform(pre[r + 1]) - uniform(pre[r]); };
+  auto next_req = [&](int r) -> int {
+    ++r;
+    while (r < B && npages(r) == 0) ++r;
+    return r;
+  };
+  auto seq_len = [&](int r) -> int {
+    const int L = seq_lens[r];
+    return L < maxp * kPageSize ? L : maxp * kPageSize;
+  };
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (uniform(pre[mid]) <= f0) lo = mid;
+    else hi = mid - 1;
+  }
+
+  const __bf16* __restrict__ qp = reinterpret_cast<const __bf16*>(a.q);
+  const __bf16* __restrict__ kpool = reinterpret_cast<const __bf16*>(a.k_pool);
+  const __bf16* __restrict__ vpool = reinterpret_cast<const __bf16*>(a.v_pool);
+  const size_t blk = (size_t)kPageSize * D;
+  auto block_ptr = [&](const __bf16* pool, int phys) -> const __bf16* {
+    return pool + ((size_t)phys * Hkv + g) * blk;
+  };
+
+  int rl = lo, jl = f0 - uniform(pre[lo]), nl = npages(lo);
+  auto advance_load = [&]() {
+    ++jl;
+    while (jl >= nl && rl + 1 < B) {
+      ++rl;
+      jl = 0;
+      nl = npages(rl);
+    }
+  };
+  auto load_id = [&]() -> int {
+    int phys = page_table[(size_t)rl * maxp + jl];
+    return phys < 0 ? 0 : (phys >= num_pages ? num_pages - 1 : phys);
+  };
+
+  int rc = lo, jc = f0 - uniform(pre[lo]), nc = npages(lo);
+  int Lc = seq_len(rc);
+
+  uint4 qv[M::kKSteps], qn[M::kKSteps];
+  load_qt<D, G>(qv, qp, Hq, rc, g, true, lane);
+  int rq = next_req(rc);
+  load_qt<D, G>(qn, qp, Hq, rq < B ? rq : B - 1, g, rq < B && uniform(pre[rq]) < f0 + nw, lane);
+
+  MState<D> st;
+  mreset<D>(st);
+
+  MBlock<D> bufs[kBufs];
+#pragma unroll
+  for (int u = 0; u < kDepth; ++u) {
+    const int phys = load_id();
+    load_mblock<D>(bufs[u], block_ptr(kpool, phys), block_ptr(vpool, phys), u < nw, lane);
+    if (u + 1 < nw) advance_load();
+  }
+  int next_phys = load_id();
+
+  int i = 0;
+#pragma unroll 1
+  for (;;) {
+#pragma unroll
+    for (int u = 0; u < kBufs; ++u) {
+      const int ahead = i + kDepth;
+      const bool more = ahead < nw;
+      const int nb = (u + kDepth) % kBufs;
+      const int phys = next_phys;
+      load_mblock<D>(bufs[nb], block_ptr(kpool, phys), block_ptr(vpool, phys), more, lane);
+      if (ahead + 1 < nw) advance_load();
+      next_phys = load_id();
+      const int live = Lc - jc * kPageSize;
+      page_mfma<D, G>(bufs[u], qv, st, live, a.scale_log2, vslot, lane);
+
+      const bool range_end = i + 1 >= nw;
+      if (jc + 1 >= nc || range_end) {
+        // ---- the wave's share of request rc is complete: write its partial
+        const float lh = head_sum<D>(st);       // head lane&15's total
+        const size_t slot = (size_t)rc + v;
+        const int qg = lane >> 4;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int hh = 4 * qg + ii;            // this lane's output row
+          const float l = __shfl(lh, hh);
+          const bool empty = !(l > 0.f);
+          const float inv = empty ? 0.f : 1.f / l;
+          if (hh < G) {
+            float* o = o_part + (slot * Hq + (size_t)g * G + hh) * D + (lane & 15);
+#pragma unroll
+            for (int bb = 0; bb < M::kDimBlocks; ++bb) o[16 * bb] = st.o[bb][ii] * inv;
+          }
+        }
+        if (qg == 0 && (lane & 15) < G) {
+          const bool empty = !(lh > 0.f);
+          lse_part[slot * Hq + (size_t)g * G + (lane & 15)] = empty ? -INFINITY : (st.m + __log2f(lh)) * kLn2;
+        }
+        if (range_end) return;
+        mreset<D>(st);
+        rc = rq;
+        jc = 0;
+        nc = npages(rc);
+        Lc = seq_len(rc);
+#pragma unroll
+        for (int c = 0; c < M::kKSteps; ++c) {
+          qv[c] = qn[c];
+          asm volatile("" : "+v"(qv[c].x), "+v"(qv[c].y), "+v"(qv[c].z), "+v"(qv[c].w)::"memory");
+        }
+        rq = next_req(rc);
+        load_qt<D, G>(qn, qp, Hq, rq < B ? rq : B - 1, g, rq < B && uniform(pre[rq]) < f0 + nw, lane);
+      } else {
+        ++jc;
+      }
+      ++i;
+    }
+  }
+}
+
+template <int D, int G>
+hipError_t launch_mfma_t(const DecodeArgs& a, hipStream_t s) {
+  const long long grid = (long long)a.num_kv_heads * (a.num_splits / kWaves);
+  if (grid <= 0 || a.num_seqs <= 0) return hipSuccess;
+  if (grid > 0x7FFFFFFFLL || a.num_splits % kWaves != 0 || a.num_seqs > kMaxBalancedSeqs)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL((decode_mfma_kernel<D, G>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, a.page_table,
+                     a.seq_lens, a.o_part, a.lse_part, a.range_meta);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_mfma_g(const DecodeArgs& a, int group, hipStream_t s) {
+  switch (group) {
+    case 1: return launch_mfma_t<D, 1>(a, s);
+    case 2: return launch_mfma_t<D, 2>(a, s);
+    case 4: return launch_mfma_t<D, 4>(a, s);
+    case 8: return launch_mfma_t<D, 8>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 template <typename T, int D, int G, bool kDense>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
   const long long grid = (long long)a.num_seqs * a.num_kv_heads * a.num_splits;
@@ -345,8 +732,8 @@ bool decode_group_supported(int group) {
 hipError_t launch_decode_balanced(const DecodeArgs& a, int dtype, int head_dim, int group,
                                   hipStream_t s) {
   if (dtype == 0) {
-    if (head_dim == 128) return launch_bal_g<__bf16, 128>(a, group, s);
-    if (head_dim == 64) return launch_bal_g<__bf16, 64>(a, group, s);
+    if (head_dim == 128) return launch_mfma_g<128>(a, group, s);
+    if (head_dim == 64) return launch_mfma_g<64>(a, group, s);
   } else if (dtype == 1) {
     if (head_dim == 128) return launch_bal_g<float, 128>(a, group, s);
     if (head_dim == 64) return launch_bal_g<float, 64>(a, group, s);

@@ -49,6 +49,7 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int group
 hipError_t launch_decode_dense(const DecodeArgs& a, int dtype, int head_dim, int group, hipStream_t s);
 // Page-balanced split: every KV head's flattened (request, page) sequence is
 // cut into a.num_splits equal wave ranges (a.num_splits a multiple of 4).
+// bf16 runs the MFMA form of the kernel, fp32 the VALU form.
 hipError_t launch_decode_balanced(const DecodeArgs& a, int dtype, int head_dim, int group,
                                   hipStream_t s);
 
