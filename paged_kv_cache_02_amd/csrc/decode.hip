@@ -478,17 +478,29 @@ __device__ __forceinline__ void page_mfma(const MBlock<D>& b, const uint4 (&qt)[
   }
   // ---- O += P V: V's B operand through the transposing LDS read (key
   // 4qg + h/4, dims 16bb + 4(h%4) .. +3 in this lane's address)
+  // the V operands are requested in batches of kBatch dim blocks ahead of
+  // their MFMAs, so a page waits for a few LDS round trips rather than one
+  // per dim block
+  constexpr int kBatch = G >= 8 ? 2 : (M::kDimBlocks >= 4 ? 4 : M::kDimBlocks);   // G = 8 has no registers to spare
   const int vkey = 4 * qg + (h >> 2);
 #pragma unroll
-  for (int bb = 0; bb < M::kDimBlocks; ++bb) {
-    const int dim = 16 * bb + 4 * (h & 3);
-    const unsigned char* pa_addr =
-        vslot + vkey * M::kRowBytes + (((dim >> 3) ^ vswz<D>(vkey)) << 4) + (dim & 7) * 2;
-    const shortx4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) shortx4_t*)(pa_addr));
-    const bf16x4_t vb = __builtin_bit_cast(bf16x4_t, r);
-    st.o[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, st.o[bb], 0, 0, 0);
-    st.o[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pb, vb, st.o[bb], 0, 0, 0);
+  for (int b0 = 0; b0 < M::kDimBlocks; b0 += kBatch) {
+    shortx4_t vr[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int dim = 16 * (b0 + k) + 4 * (h & 3);
+      const unsigned char* pa_addr =
+          vslot + vkey * M::kRowBytes + (((dim >> 3) ^ vswz<D>(vkey)) << 4) + (dim & 7) * 2;
+      vr[k] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) shortx4_t*)(pa_addr));
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const bf16x4_t vb = __builtin_bit_cast(bf16x4_t, vr[k]);
+      st.o[b0 + k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, st.o[b0 + k], 0, 0, 0);
+      st.o[b0 + k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pb, vb, st.o[b0 + k], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x0100, kBatch, 0);      // the batch's transposing reads
+    __builtin_amdgcn_sched_group_barrier(0x0008, 2 * kBatch, 0);  // then its MFMAs
   }
 }
 
