@@ -1,9 +1,9 @@
 // Paged decode attention and its split-K partitions (gfx950).
 //
-// Kernels: decode_kernel (one workgroup per (request, KV head, split), VALU,
-// bf16 and fp32), decode_balanced_kernel (the page-balanced split, VALU:
-// fp32), and decode_mfma_kernel (the page-balanced split with both
-// contractions on MFMA: bf16).
+// Kernels: decode_kernel / decode_split_mfma_kernel (one workgroup per
+// (request, KV head, split): VALU for fp32, MFMA for bf16) and
+// decode_balanced_kernel / decode_mfma_kernel (the page-balanced split: VALU
+// for fp32, MFMA for bf16).
 //
 // One workgroup owns one (request, KV head, split) triple, so the G query
 // heads of a GQA group share every K/V page load (GQA: week-1 material of the
@@ -328,191 +328,6 @@ decode_balanced_kernel(DecodeArgs a, const int32_t* __restrict__ page_table,
 // are padding whose results are never written.
 // ---------------------------------------------------------------------------
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef short shortx4_t __attribute__((ext_vector_type(4)));
-typedef float floatx4_t __attribute__((ext_vector_type(4)));
-
-template <int D>
-struct MShape {
-  static constexpr int kKSteps = D / 32;                // 16x16x32 steps of S^T
-  static constexpr int kDimBlocks = D / 16;             // 16-dim output blocks of O
-  static constexpr int kRowBytes = D * 2;               // one key row (bf16)
-  static constexpr int kChunks = D / 8;                 // 16-byte chunks per key row
-  static constexpr int kVLoads = kPageSize * D * 2 / 1024;   // 1 KB wave loads per V block
-  static constexpr int kKeysPerVLoad = 1024 / kRowBytes;
-};
-
-// XOR swizzle of a key row's 16-byte chunks in the LDS slot (bit 0 left
-// alone: the two chunks of one 16-dim block differ in it).
-template <int D>
-__device__ __forceinline__ int vswz(int key) {
-  return D == 128 ? ((key & 7) << 1) : (((key >> 1) & 3) << 1);
-}
-
-template <int D>
-struct MBlock {  // one (page, KV head) block in registers: K as the S^T A operand, V as loaded
-  uint4 k[MShape<D>::kKSteps];
-  uint4 v[MShape<D>::kVLoads];
-};
-
-template <int D>
-__device__ __forceinline__ void load_mblock(MBlock<D>& b, const __bf16* kblk, const __bf16* vblk, bool live,
-                                            int lane) {
-  using M = MShape<D>;
-  const int bytes = live ? kPageSize * M::kRowBytes : 0;
-  const __amdgpu_buffer_rsrc_t rk =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(kblk), (short)0, bytes, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t rv =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(vblk), (short)0, bytes, kBufferWord3);
-#pragma unroll
-  for (int c = 0; c < M::kKSteps; ++c) {
-    const int off = (lane & 15) * M::kRowBytes + (32 * c + 8 * (lane >> 4)) * 2;
-    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, kLoadNontemporal);
-    b.k[c] = make_uint4(x[0], x[1], x[2], x[3]);
-  }
-#pragma unroll
-  for (int t = 0; t < M::kVLoads; ++t) {
-    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rv, t * 1024 + lane * 16, 0, kLoadNontemporal);
-    b.v[t] = make_uint4(x[0], x[1], x[2], x[3]);
-  }
-}
-
-template <int D>
-struct MState {
-  floatx4_t o[MShape<D>::kDimBlocks];   // lane j, reg i: head 4(j/16)+i, dim 16b + j%16
-  float m;                              // running max of head j%16 (log2 units)
-  float l;                              // this lane's part of head j%16's running sum
-};
-
-template <int D>
-__device__ __forceinline__ void mreset(MState<D>& st) {
-#pragma unroll
-  for (int b = 0; b < MShape<D>::kDimBlocks; ++b) st.o[b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  st.m = -INFINITY;
-  st.l = 0.f;
-}
-
-// Q^T for one (row, KV head): lane j holds head j%16's dims 32c + 8(j/16)
-// .. +7; heads at or past G read zeros (the resource covers G heads).
-template <int D, int G>
-__device__ __forceinline__ void load_qt(uint4 (&qt)[MShape<D>::kKSteps], const __bf16* q, int Hq, int row,
-                                        int g, bool valid, int lane) {
-  using M = MShape<D>;
-  const __bf16* base = q + ((size_t)row * Hq + (size_t)g * G) * D;
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<__bf16*>(base), (short)0, valid ? G * M::kRowBytes : 0, kBufferWord3);
-#pragma unroll
-  for (int c = 0; c < M::kKSteps; ++c) {
-    const int off = (lane & 15) * M::kRowBytes + (32 * c + 8 * (lane >> 4)) * 2;
-    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
-    qt[c] = make_uint4(x[0], x[1], x[2], x[3]);
-  }
-}
-
-template <int D, int G>
-__device__ __forceinline__ void page_mfma(const MBlock<D>& b, const uint4 (&qt)[MShape<D>::kKSteps],
-                                          MState<D>& st, int live, float scale_log2,
-                                          unsigned char* vslot, int lane) {
-  using M = MShape<D>;
-  const int qg = lane >> 4;
-  const int h = lane & 15;
-  // ---- S^T = K Q^T
-  floatx4_t s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int c = 0; c < M::kKSteps; ++c)
-    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b.k[c]),
-                                                __builtin_bit_cast(bf16x8_t, qt[c]), s, 0, 0, 0);
-  // ---- V into the wave's LDS slot; keys at or past `live` (possibly NaN)
-  // become zeros
-#pragma unroll
-  for (int t = 0; t < M::kVLoads; ++t) {
-    const int key = t * M::kKeysPerVLoad + lane / M::kChunks;
-    const int chunk = lane % M::kChunks;
-    uint4 x = b.v[t];
-    const bool ok = key < live;
-    x.x = ok ? x.x : 0u;
-    x.y = ok ? x.y : 0u;
-    x.z = ok ? x.z : 0u;
-    x.w = ok ? x.w : 0u;
-    *reinterpret_cast<uint4*>(vslot + key * M::kRowBytes + ((chunk ^ vswz<D>(key)) << 4)) = x;
-  }
-  // ---- online softmax of head h over keys 4qg .. 4qg + 3 of the page
-  float x[4];
-  float xm = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[i] = (4 * qg + i < live && h < G) ? s[i] * scale_log2 : -INFINITY;
-    xm = fmaxf(xm, x[i]);
-  }
-  xm = fmaxf(xm, __shfl_xor(xm, 16));
-  xm = fmaxf(xm, __shfl_xor(xm, 32));
-  if (__builtin_expect(__any(xm > st.m + kRescaleLog2), 0)) {
-    const float mn = fmaxf(st.m, xm);
-    const float alpha = (mn == st.m) ? 1.f : fast_exp2(st.m - mn);
-    st.l *= alpha;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float ai = __shfl(alpha, 4 * qg + i);   // output row 4qg + i is head 4qg + i
-#pragma unroll
-      for (int bb = 0; bb < M::kDimBlocks; ++bb) st.o[bb][i] *= ai;
-    }
-    st.m = mn;
-  }
-  const float mref = st.m == -INFINITY ? 0.f : st.m;
-  float p[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    p[i] = x[i] == -INFINITY ? 0.f : fast_exp2(x[i] - mref);
-    st.l += p[i];
-  }
-  // p as the sum of two bf16 parts: a single bf16 rounding (2^-9 relative)
-  // would move outputs of a few keys by up to |v| * 2^-9, which with
-  // |v| ~ 4 is a bf16 output step; with hi + lo the products keep about 16
-  // bits, and V itself is exact
-  bf16x4_t pa, pb;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    pa[i] = (__bf16)p[i];
-    pb[i] = (__bf16)(p[i] - (float)pa[i]);
-  }
-  // ---- O += P V: V's B operand through the transposing LDS read (key
-  // 4qg + h/4, dims 16bb + 4(h%4) .. +3 in this lane's address)
-  // the V operands are requested in batches of kBatch dim blocks ahead of
-  // their MFMAs, so a page waits for a few LDS round trips rather than one
-  // per dim block
-  constexpr int kBatch = G >= 8 ? 2 : (M::kDimBlocks >= 4 ? 4 : M::kDimBlocks);   // G = 8 has no registers to spare
-  const int vkey = 4 * qg + (h >> 2);
-#pragma unroll
-  for (int b0 = 0; b0 < M::kDimBlocks; b0 += kBatch) {
-    shortx4_t vr[kBatch];
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const int dim = 16 * (b0 + k) + 4 * (h & 3);
-      const unsigned char* pa_addr =
-          vslot + vkey * M::kRowBytes + (((dim >> 3) ^ vswz<D>(vkey)) << 4) + (dim & 7) * 2;
-      vr[k] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) shortx4_t*)(pa_addr));
-    }
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const bf16x4_t vb = __builtin_bit_cast(bf16x4_t, vr[k]);
-      st.o[b0 + k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, st.o[b0 + k], 0, 0, 0);
-      st.o[b0 + k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pb, vb, st.o[b0 + k], 0, 0, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x0100, kBatch, 0);      // the batch's transposing reads
-    __builtin_amdgcn_sched_group_barrier(0x0008, 2 * kBatch, 0);  // then its MFMAs
-  }
-}
-
-// Head totals at a request's end: l summed over the head's four lanes.
-template <int D>
-__device__ __forceinline__ float head_sum(const MState<D>& st) {
-  float l = st.l;
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  return l;
-}
-
 template <int D, int G>
 __global__ void __launch_bounds__(kThreads, 2)
 decode_mfma_kernel(DecodeArgs a, const int32_t* __restrict__ page_table,
@@ -693,12 +508,34 @@ hipError_t launch_mfma_g(const DecodeArgs& a, int group, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+// decode_kernel with the page work on MFMA (bf16).
+template <int D, int G, bool kDense>
+__global__ void __launch_bounds__(kThreads, 2)
+decode_split_mfma_kernel(DecodeArgs a) {
+  const int nsplit = a.num_splits;
+  const int bid = blockIdx.x;
+  const int g = bid % a.num_kv_heads;
+  const int rs = bid / a.num_kv_heads;
+  const int split = rs % nsplit;
+  const int r = rs / nsplit;
+  const int L = a.seq_lens[r];
+  int npages = (L + kPageSize - 1) / kPageSize;
+  npages = npages < a.max_pages_per_seq ? npages : a.max_pages_per_seq;
+  const int pps = (npages + nsplit - 1) / nsplit;
+  const int pb = split * pps;
+  const int pe = (pb + pps) < npages ? (pb + pps) : npages;
+  decode_range_mfma<D, G, kDense>(a, r, r, g, split, pb, pe, L);
+}
+
 template <typename T, int D, int G, bool kDense>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
   const long long grid = (long long)a.num_seqs * a.num_kv_heads * a.num_splits;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((decode_kernel<T, D, G, kDense>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  if constexpr (sizeof(T) == 2)
+    hipLaunchKernelGGL((decode_split_mfma_kernel<D, G, kDense>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<T, D, G, kDense>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

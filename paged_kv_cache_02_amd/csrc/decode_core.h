@@ -338,6 +338,200 @@ struct Pipe {
   static constexpr int kBufs = kDepth + 1;
 };
 
+// ---------------------------------------------------------------------------
+// The (page, KV head) block on MFMA (bf16): S^T = K Q^T with
+// v_mfma_f32_16x16x32_bf16 (lane j holds key j%16, dims 32c + 8(j/16) .. +7
+// of k-step c; the G query heads sit in the 16 columns of Q^T, the others
+// load zeros), whose result (lane j: keys 4(j/16) .. +3 of head j%16) is
+// the A operand of O += P V with v_mfma_f32_16x16x16bf16_1k; V's B operand
+// comes from the wave's own LDS slot through ds_read_b64_tr_b16.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef short shortx4_t __attribute__((ext_vector_type(4)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+template <int D>
+struct MShape {
+  static constexpr int kKSteps = D / 32;                // 16x16x32 steps of S^T
+  static constexpr int kDimBlocks = D / 16;             // 16-dim output blocks of O
+  static constexpr int kRowBytes = D * 2;               // one key row (bf16)
+  static constexpr int kChunks = D / 8;                 // 16-byte chunks per key row
+  static constexpr int kVLoads = kPageSize * D * 2 / 1024;   // 1 KB wave loads per V block
+  static constexpr int kKeysPerVLoad = 1024 / kRowBytes;
+};
+
+// XOR swizzle of a key row's 16-byte chunks in the LDS slot (bit 0 left
+// alone: the two chunks of one 16-dim block differ in it).
+template <int D>
+__device__ __forceinline__ int vswz(int key) {
+  return D == 128 ? ((key & 7) << 1) : (((key >> 1) & 3) << 1);
+}
+
+template <int D>
+struct MBlock {  // one (page, KV head) block in registers: K as the S^T A operand, V as loaded
+  uint4 k[MShape<D>::kKSteps];
+  uint4 v[MShape<D>::kVLoads];
+};
+
+template <int D>
+__device__ __forceinline__ void load_mblock(MBlock<D>& b, const __bf16* kblk, const __bf16* vblk, bool live,
+                                            int lane) {
+  using M = MShape<D>;
+  const int bytes = live ? kPageSize * M::kRowBytes : 0;
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(kblk), (short)0, bytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(vblk), (short)0, bytes, kBufferWord3);
+#pragma unroll
+  for (int c = 0; c < M::kKSteps; ++c) {
+    const int off = (lane & 15) * M::kRowBytes + (32 * c + 8 * (lane >> 4)) * 2;
+    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, kLoadNontemporal);
+    b.k[c] = make_uint4(x[0], x[1], x[2], x[3]);
+  }
+#pragma unroll
+  for (int t = 0; t < M::kVLoads; ++t) {
+    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rv, t * 1024 + lane * 16, 0, kLoadNontemporal);
+    b.v[t] = make_uint4(x[0], x[1], x[2], x[3]);
+  }
+}
+
+template <int D>
+struct MState {
+  floatx4_t o[MShape<D>::kDimBlocks];   // lane j, reg i: head 4(j/16)+i, dim 16b + j%16
+  float m;                              // running max of head j%16 (log2 units)
+  float l;                              // this lane's part of head j%16's running sum
+};
+
+template <int D>
+__device__ __forceinline__ void mreset(MState<D>& st) {
+#pragma unroll
+  for (int b = 0; b < MShape<D>::kDimBlocks; ++b) st.o[b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  st.m = -INFINITY;
+  st.l = 0.f;
+}
+
+// Q^T for one (row, KV head): lane j holds head j%16's dims 32c + 8(j/16)
+// .. +7; heads at or past G read zeros (the resource covers G heads).
+template <int D, int G>
+__device__ __forceinline__ void load_qt(uint4 (&qt)[MShape<D>::kKSteps], const __bf16* q, int Hq, int row,
+                                        int g, bool valid, int lane) {
+  using M = MShape<D>;
+  const __bf16* base = q + ((size_t)row * Hq + (size_t)g * G) * D;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<__bf16*>(base), (short)0, valid ? G * M::kRowBytes : 0, kBufferWord3);
+#pragma unroll
+  for (int c = 0; c < M::kKSteps; ++c) {
+    const int off = (lane & 15) * M::kRowBytes + (32 * c + 8 * (lane >> 4)) * 2;
+    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+    qt[c] = make_uint4(x[0], x[1], x[2], x[3]);
+  }
+}
+
+template <int D, int G>
+__device__ __forceinline__ void page_mfma(const MBlock<D>& b, const uint4 (&qt)[MShape<D>::kKSteps],
+                                          MState<D>& st, int live, float scale_log2,
+                                          unsigned char* vslot, int lane) {
+  using M = MShape<D>;
+  const int qg = lane >> 4;
+  const int h = lane & 15;
+  // ---- S^T = K Q^T
+  floatx4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < M::kKSteps; ++c)
+    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b.k[c]),
+                                                __builtin_bit_cast(bf16x8_t, qt[c]), s, 0, 0, 0);
+  // ---- V into the wave's LDS slot; keys at or past `live` (possibly NaN)
+  // become zeros
+#pragma unroll
+  for (int t = 0; t < M::kVLoads; ++t) {
+    const int key = t * M::kKeysPerVLoad + lane / M::kChunks;
+    const int chunk = lane % M::kChunks;
+    uint4 x = b.v[t];
+    const bool ok = key < live;
+    x.x = ok ? x.x : 0u;
+    x.y = ok ? x.y : 0u;
+    x.z = ok ? x.z : 0u;
+    x.w = ok ? x.w : 0u;
+    *reinterpret_cast<uint4*>(vslot + key * M::kRowBytes + ((chunk ^ vswz<D>(key)) << 4)) = x;
+  }
+  // ---- online softmax of head h over keys 4qg .. 4qg + 3 of the page
+  float x[4];
+  float xm = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = (4 * qg + i < live && h < G) ? s[i] * scale_log2 : -INFINITY;
+    xm = fmaxf(xm, x[i]);
+  }
+  xm = fmaxf(xm, __shfl_xor(xm, 16));
+  xm = fmaxf(xm, __shfl_xor(xm, 32));
+  if (__builtin_expect(__any(xm > st.m + kRescaleLog2), 0)) {
+    const float mn = fmaxf(st.m, xm);
+    const float alpha = (mn == st.m) ? 1.f : fast_exp2(st.m - mn);
+    st.l *= alpha;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float ai = __shfl(alpha, 4 * qg + i);   // output row 4qg + i is head 4qg + i
+#pragma unroll
+      for (int bb = 0; bb < M::kDimBlocks; ++bb) st.o[bb][i] *= ai;
+    }
+    st.m = mn;
+  }
+  const float mref = st.m == -INFINITY ? 0.f : st.m;
+  float p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    p[i] = x[i] == -INFINITY ? 0.f : fast_exp2(x[i] - mref);
+    st.l += p[i];
+  }
+  // p as the sum of two bf16 parts: a single bf16 rounding (2^-9 relative)
+  // would move outputs of a few keys by up to |v| * 2^-9, which with
+  // |v| ~ 4 is a bf16 output step; with hi + lo the products keep about 16
+  // bits, and V itself is exact
+  bf16x4_t pa, pb;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    pa[i] = (__bf16)p[i];
+    pb[i] = (__bf16)(p[i] - (float)pa[i]);
+  }
+  // ---- O += P V: V's B operand through the transposing LDS read (key
+  // 4qg + h/4, dims 16bb + 4(h%4) .. +3 in this lane's address)
+  // the V operands are requested in batches of kBatch dim blocks ahead of
+  // their MFMAs, so a page waits for a few LDS round trips rather than one
+  // per dim block
+  constexpr int kBatch = G >= 8 ? 2 : (M::kDimBlocks >= 4 ? 4 : M::kDimBlocks);   // G = 8 has no registers to spare
+  const int vkey = 4 * qg + (h >> 2);
+#pragma unroll
+  for (int b0 = 0; b0 < M::kDimBlocks; b0 += kBatch) {
+    shortx4_t vr[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int dim = 16 * (b0 + k) + 4 * (h & 3);
+      const unsigned char* pa_addr =
+          vslot + vkey * M::kRowBytes + (((dim >> 3) ^ vswz<D>(vkey)) << 4) + (dim & 7) * 2;
+      vr[k] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) shortx4_t*)(pa_addr));
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const bf16x4_t vb = __builtin_bit_cast(bf16x4_t, vr[k]);
+      st.o[b0 + k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, st.o[b0 + k], 0, 0, 0);
+      st.o[b0 + k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pb, vb, st.o[b0 + k], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x0100, kBatch, 0);      // the batch's transposing reads
+    __builtin_amdgcn_sched_group_barrier(0x0008, 2 * kBatch, 0);  // then its MFMAs
+  }
+}
+
+// Head totals at a request's end: l summed over the head's four lanes.
+template <int D>
+__device__ __forceinline__ float head_sum(const MState<D>& st) {
+  float l = st.l;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  return l;
+}
+
+
 // One (request r, KV head g) over the request's logical pages [pb, pe), the
 // pages dealt round-robin to the workgroup's kW waves (64 * kW threads).
 // Each wave keeps its own online-softmax state; the states are merged
@@ -505,6 +699,122 @@ pages_done:
     if (!a.write_partials) {
       T* out = reinterpret_cast<T*>(a.out);
       out[((size_t)qrow * Hq + hq) * D + dim] = from_float<T>(o);
+      if (a.lse != nullptr && dim == 0) a.lse[(size_t)qrow * Hq + hq] = lse2;
+    } else {
+      const size_t row = ((size_t)qrow * Hq + hq) * nsplit + split;
+      a.o_part[row * D + dim] = o;
+      if (dim == 0) a.lse_part[row] = lse2;
+    }
+  }
+}
+
+// decode_range with the page work on MFMA (bf16, 4 waves): the same page
+// walk and LDS merge, with each wave's state in the MFMA layout (output
+// rows = query heads) and a 4 KB LDS slot per wave for V's transposing
+// reads.
+template <int D, int G, bool kDense>
+__device__ __forceinline__ void decode_range_mfma(const DecodeArgs& a, int r, int qrow, int g, int split,
+                                                  int pb, int pe, int L) {
+  using M = MShape<D>;
+  constexpr int kW = 4;
+  constexpr int kDepth = 3;
+  constexpr int kBufs = kDepth + 1;
+  __shared__ __align__(16) unsigned char vslots[kW][kPageSize * M::kRowBytes];
+  const int32_t num_pages = a.num_pages;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nsplit = a.num_splits;
+  const int Hq = a.num_q_heads;
+  const int Hkv = a.num_kv_heads;
+  const __bf16* __restrict__ qp = reinterpret_cast<const __bf16*>(a.q);
+  const __bf16* __restrict__ kpool = reinterpret_cast<const __bf16*>(a.k_pool);
+  const __bf16* __restrict__ vpool = reinterpret_cast<const __bf16*>(a.v_pool);
+  const int32_t* __restrict__ ptab = kDense ? nullptr : a.page_table + (size_t)r * a.max_pages_per_seq;
+
+  uint4 qt[M::kKSteps];
+  load_qt<D, G>(qt, qp, Hq, qrow, g, true, lane);
+  MState<D> st;
+  mreset<D>(st);
+
+  const size_t blk = (size_t)kPageSize * D;
+  const int first = pb + wave;
+  const int nw = first < pe ? (pe - first + kW - 1) / kW : 0;
+  auto page_id = [&](int i) -> int {
+    const int ic = i < nw ? i : nw - 1;
+    if (kDense) return first + kW * ic;
+    int phys = ptab[first + kW * ic];
+    return phys < 0 ? 0 : (phys >= num_pages ? num_pages - 1 : phys);
+  };
+  auto block_ptr = [&](const __bf16* pool, int phys) -> const __bf16* {
+    if (kDense) return pool + (((size_t)r * Hkv + g) * a.max_pages_per_seq + phys) * blk;
+    return pool + ((size_t)phys * Hkv + g) * blk;
+  };
+  if (nw > 0) {
+    MBlock<D> bufs[kBufs];
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u) {
+      const int phys = page_id(u);
+      load_mblock<D>(bufs[u], block_ptr(kpool, phys), block_ptr(vpool, phys), u < nw, lane);
+    }
+    int next_phys = page_id(kDepth);
+    int i = 0;
+#pragma unroll 1
+    for (;;) {
+#pragma unroll
+      for (int u = 0; u < kBufs; ++u) {
+        const int ahead = i + kDepth;
+        const int nb = (u + kDepth) % kBufs;
+        const int phys = next_phys;
+        load_mblock<D>(bufs[nb], block_ptr(kpool, phys), block_ptr(vpool, phys), ahead < nw, lane);
+        next_phys = page_id(ahead + 1);
+        const int live = L - (first + kW * i) * kPageSize;
+        page_mfma<D, G>(bufs[u], qt, st, live, a.scale_log2, vslots[wave], lane);
+        if (++i >= nw) goto pages_done;
+      }
+    }
+  }
+pages_done:
+
+  // ---- merge the waves through LDS (heads' totals, rows in [head][dim])
+  const float lh = head_sum<D>(st);
+  __shared__ float sm_m[kW][G];
+  __shared__ float sm_l[kW][G];
+  __shared__ float sm_acc[kW][G][D];
+  if (lane < G) {
+    sm_m[wave][lane] = st.m;
+    sm_l[wave][lane] = lh;
+  }
+  const int qg = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hh = 4 * qg + i;
+    if (hh < G) {
+#pragma unroll
+      for (int bb = 0; bb < M::kDimBlocks; ++bb) sm_acc[wave][hh][16 * bb + (lane & 15)] = st.o[bb][i];
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * D; idx += 64 * kW) {
+    const int h = idx / D;
+    const int dim = idx % D;
+    float Mt = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kW; ++w) Mt = fmaxf(Mt, sm_m[w][h]);
+    float lt = 0.f, ot = 0.f;
+#pragma unroll
+    for (int w = 0; w < kW; ++w) {
+      const float mw = sm_m[w][h];
+      const float f = (mw == -INFINITY) ? 0.f : fast_exp2(mw - Mt);
+      lt += f * sm_l[w][h];
+      ot += f * sm_acc[w][h][dim];
+    }
+    const int hq = g * G + h;
+    const bool empty = !(lt > 0.f);
+    const float o = empty ? 0.f : ot / lt;
+    const float lse2 = empty ? -INFINITY : (Mt + __log2f(lt)) * kLn2;
+    if (!a.write_partials) {
+      __bf16* out = reinterpret_cast<__bf16*>(a.out);
+      out[((size_t)qrow * Hq + hq) * D + dim] = (__bf16)o;
       if (a.lse != nullptr && dim == 0) a.lse[(size_t)qrow * Hq + hq] = lse2;
     } else {
       const size_t row = ((size_t)qrow * Hq + hq) * nsplit + split;
