@@ -10,7 +10,7 @@
 // One wave per (row, head): lanes read the S partial lse values (strided by
 // 64), reduce max and sum with wave shuffles, then each lane produces d/64 of
 // the output dims, reading the S partial rows coalesced, eight partials per
-// batch of loads.  Partials come
+// batch of loads; the first batch is requested together with the lse values.  Partials come
 // either S per (row, head) (equal splits) or as a variable run of slots per
 // row given by a range table (page-balanced splits).
 #include "pa_internal.h"
@@ -65,13 +65,27 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) merge_kernel(MergeArgs a)
   }
   const float* lp = a.lse_part;
   const float* op = a.o_part;
+  constexpr int kPer = D / 64;
+  constexpr int kBatch = 8;   // partial rows requested together
 
-  float M = -INFINITY;
-  for (int s = lane; s < S; s += 64) M = fmaxf(M, lp[base + s * step]);
+  // The first batch of partial rows is requested together with the lse
+  // values (it does not depend on them), so a (row, head) with at most
+  // kBatch partials waits for one memory round trip after the range table.
+  float o0[kBatch][kPer];
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j) {
+    const long long row = base + (long long)(j < S ? j : 0) * step;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) o0[j][i] = j < S ? op[row * D + lane + 64 * i] : 0.f;
+  }
+  const float v_lane = lane < S ? lp[base + (long long)lane * step] : -INFINITY;   // slot `lane`'s lse
+
+  float M = v_lane;
+  for (int s = lane + 64; s < S; s += 64) M = fmaxf(M, lp[base + s * step]);
   M = wave_max(M);
   const float Mb = (M == -INFINITY) ? 0.f : M;   // all splits empty: weights stay 0
-  float tot = 0.f;
-  for (int s = lane; s < S; s += 64) {
+  float tot = (v_lane == -INFINITY) ? 0.f : exp2f((v_lane - Mb) * kLog2e);
+  for (int s = lane + 64; s < S; s += 64) {
     const float v = lp[base + s * step];
     tot += (v == -INFINITY) ? 0.f : exp2f((v - Mb) * kLog2e);
   }
@@ -79,15 +93,20 @@ __global__ void __launch_bounds__(64 * kWavesPerBlock) merge_kernel(MergeArgs a)
   const bool empty = !(tot > 0.f);
   const float LSE = empty ? -INFINITY : Mb + logf(tot);
 
-  constexpr int kPer = D / 64;
-  constexpr int kBatch = 8;   // partial rows requested together
   float acc[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) acc[i] = 0.f;
   if (!empty) {
-    // the rows of kBatch partials (and their lse) are requested before any
-    // is used, so the loop waits for one memory round trip per batch
-    for (int s0 = 0; s0 < S; s0 += kBatch) {
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const float v = __shfl(v_lane, j);
+      const float w = (v == -INFINITY) ? 0.f : exp2f((v - LSE) * kLog2e);
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) acc[i] = fmaf(w, o0[j][i], acc[i]);
+    }
+    // the rows of the later batches (and their lse) are requested a batch
+    // at a time, before any is used
+    for (int s0 = kBatch; s0 < S; s0 += kBatch) {
       float v[kBatch];
       float o[kBatch][kPer];
 #pragma unroll
