@@ -287,6 +287,35 @@ def test_balanced_at_the_request_limit():
     compare(b, out, lse, ro, rl, label="balanced, 4096 requests")
 
 
+def test_past_the_request_limit_falls_back_to_one_workgroup_per_request():
+    # one request more than the page-balanced kernel takes: the guard picks
+    # one workgroup per (request, KV head) with no split and no merge pass
+    rng = np.random.default_rng(67)
+    lens = rng.integers(1, 65, size=4097)
+    b = ragged(67, lens, 16, 8, 128)
+    dev = device_batch(b)
+    plan = guard_path(b, dev)
+    print(f"case 4097 requests plan={plan}", flush=True)
+    assert plan["path"] == "decode" and plan["num_splits"] == 1
+    out, lse = run_decode(b, dev)
+    pick = np.unique(np.concatenate([[0, 1, 2048, 4095, 4096], rng.choice(4097, 40, replace=False)]))
+    ro, rl = oracle_run(b, requests=pick)
+    compare(b, out, lse, ro, rl, rows=pick, label="fallback, 4097 requests, sampled")
+
+
+def test_too_little_work_falls_back_to_equal_splits():
+    # two requests whose pages are far fewer than the balanced kernel's wave
+    # ranges: the guard splits each (request, KV head) in two and merges
+    b = ragged(68, [700, 33], 32, 8, 128)
+    dev = device_batch(b)
+    plan = guard_path(b, dev)
+    print(f"case 2 requests plan={plan}", flush=True)
+    assert plan["path"] == "decode_split" and plan["num_splits"] == 2
+    ro, rl = oracle_run(b)
+    out, lse = run_decode(b, dev)
+    compare(b, out, lse, ro, rl, label="fallback, 2 requests, 2 splits")
+
+
 def test_balanced_fewer_pages_than_waves():
     # the declared bound admits long contexts, the actual ones hold 11 pages:
     # most waves own no page, a few own one
