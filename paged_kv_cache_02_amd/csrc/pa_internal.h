@@ -43,6 +43,8 @@ struct DecodeArgs {
 
 // dtype: 0 = bf16, 1 = fp32.  Returns hipSuccess or the launch error.
 bool decode_group_supported(int group);
+// One workgroup per (request, KV head, split); bf16 runs the MFMA form of
+// the page step, fp32 the VALU form.
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int group, hipStream_t s);
 // The per-(request, KV head) kernel over a dense cache [B, Hkv, MP * P, d]
 // (a.page_table unused; a.max_pages_per_seq = capacity in pages; unsplit).
