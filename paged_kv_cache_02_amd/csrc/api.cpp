@@ -17,11 +17,16 @@ namespace {
 // --------------------------------------------------------------------------
 // dispatch-guard tuning constants
 // --------------------------------------------------------------------------
-// Page-balanced decode: resident decode workgroups per CU the grid is sized
-// for (two waves per SIMD, which every decode kernel instance reaches), so
-// the whole grid is one round and all of its waves carry equal page counts.
-constexpr int kDecodeWgsPerCu = 2;
+// Page-balanced decode: workgroups of 4 waves per CU the grid is sized for,
+// so the whole grid is one round and all of its waves carry equal page
+// counts.  Each wave of the bf16 (MFMA) kernel keeps 3 pages of K and V in
+// flight; its rate was best at about 96 KB in flight per CU (measured on
+// the mixed step, Qwen3-4B and Qwen3-0.6B shapes, d = 128, and the long
+// d = 64 one), so one workgroup per CU when a (page, KV head) block of K
+// and V is 8 KB or more, else two (which every decode kernel instance can
+// hold: two waves per SIMD).  The fp32 (VALU) kernel keeps two.
 constexpr int kWavesPerDecodeWg = 4;
+constexpr int kBlockBytesOneWg = 8192;
 // Fallback equal-split decode (more than pa::kMaxBalancedSeqs requests, or too
 // little work to spread): split until the grid holds about this many
 // workgroups per CU, so that uneven context lengths still leave every CU busy.
@@ -130,8 +135,13 @@ pa::DecodeArgs decode_args(const pa_desc* d, const void* q, const void* k_pool, 
 
 // Page-balanced decode: V wave ranges per KV head; workspace holds the
 // partials of B + V - 1 slots and the [B, 2] range table.
+int decode_wgs_per_cu(const pa_desc* d) {
+  if (d->dtype != PA_BF16) return 2;
+  const long long block = 2LL * d->page_size * d->head_dim * 2;
+  return block >= kBlockBytesOneWg ? 1 : 2;
+}
 int balanced_ranges(const pa_desc* d, int cus) {
-  long long wgs = (long long)cus * kDecodeWgsPerCu / d->num_kv_heads;
+  long long wgs = (long long)cus * decode_wgs_per_cu(d) / d->num_kv_heads;
   if (wgs < 1) wgs = 1;
   if (wgs > (1 << 20)) wgs = 1 << 20;
   return (int)(wgs * kWavesPerDecodeWg);

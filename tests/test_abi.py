@@ -49,15 +49,22 @@ def align256(x):
 
 
 def test_plan_balanced_decode_sizes_one_round_of_waves():
-    # 2 workgroups of 4 waves per CU, shared evenly by the KV heads
+    # bf16, d = 128 (8 KB K/V blocks): one workgroup of 4 waves per CU,
+    # shared evenly by the KV heads
     d3 = desc(B=64, Hq=32, Hkv=8, NP=20000, MP=512, max_seq_len=8192)
     p3 = pa.pa_plan(d3, cu_count=256)
-    V = 4 * (2 * 256 // 8)
+    V = 4 * (256 // 8)
     assert p3["path"] == "decode_balanced" and p3["num_splits"] == V
-    assert p3["grid_x"] == 8 * V // 4 == 2 * 256
+    assert p3["grid_x"] == 8 * V // 4 == 256
     slots = 64 + V - 1
     assert p3["workspace_bytes"] == (align256(slots * 32 * 128 * 4) + align256(slots * 32 * 4) +
                                      align256(64 * 2 * 4))
+    # bf16, d = 64 (4 KB blocks) and fp32: two workgroups per CU
+    for dd in (desc(B=64, Hq=32, Hkv=8, d=64, NP=20000, MP=512, max_seq_len=8192),
+               desc(B=64, Hq=32, Hkv=8, NP=20000, MP=512, max_seq_len=8192, dtype=pa.PA_F32)):
+        p = pa.pa_plan(dd, cu_count=256)
+        assert p["path"] == "decode_balanced" and p["num_splits"] == 4 * (2 * 256 // 8)
+        assert p["grid_x"] == 2 * 256
     # more KV heads than workgroup slots: one workgroup (4 wave ranges) per head
     many = desc(B=8, Hq=1024, Hkv=1024, NP=5000, MP=512, max_seq_len=8192)
     pm = pa.pa_plan(many, cu_count=256)
