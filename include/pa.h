@@ -114,8 +114,9 @@ typedef struct pa_plan_info {
  * one page per wave (B * ceil(max_seq_len / P) >= num_splits): every KV
  * head's pages, taken in (request, page) order, are cut into num_splits
  * (= V) equal wave ranges, grid_x = Hkv * V / 4 workgroups (one resident
- * round: two per compute unit), each wave writes a partial per request it
- * touches and a merge pass combines them by log-sum-exp.  Otherwise decode
+ * round: one per compute unit for bf16 with 2 * P * d * 2 >= 8192 bytes of
+ * K and V per (page, KV head), else two), each wave writes a partial per
+ * request it touches and a merge pass combines them by log-sum-exp.  Otherwise decode
  * runs one workgroup per (request, KV head), split into S equal partitions
  * (PA_PATH_DECODE_SPLIT) when B*Hkv workgroups would leave the chip's
  * cu_count compute units under-filled and the contexts are long enough.
