@@ -336,9 +336,9 @@ decode_mfma_kernel(DecodeArgs a, const int32_t* __restrict__ page_table,
   using M = MShape<D>;
   static_assert(G <= 16, "at most 16 query heads per KV head");
   // pages whose K/V loads are in flight ahead of the one computed: with one
-  // workgroup per CU at d = 128 (8 KB blocks) two measured slightly faster
-  // than three; d = 64 runs two workgroups per CU with three
-  constexpr int kDepth = D >= 128 ? 2 : 3;
+  // workgroup per CU at d = 128 (8 KB blocks) one measured as fast as two
+  // or three, or 1-2% faster; d = 64 runs two workgroups per CU with three
+  constexpr int kDepth = D >= 128 ? 1 : 3;
   constexpr int kBufs = kDepth + 1;
   __shared__ int pre[kMaxBalancedSeqs + 1];
   __shared__ __align__(16) unsigned char vslots[kWaves][kPageSize * M::kRowBytes];
