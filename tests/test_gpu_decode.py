@@ -388,7 +388,10 @@ def test_balanced_workspace_reuse_and_leftover_contents():
                                             (32, 8, 64, W.BF16), (64, 8, 128, W.BF16),
                                             (64, 8, 64, W.BF16), (64, 64, 128, W.BF16),
                                             (16, 2, 128, W.BF16), (16, 4, 64, W.F32),
-                                            (8, 2, 128, W.F32)])
+                                            (8, 2, 128, W.F32),
+                                            # KV head counts that do not divide the CU count:
+                                            # wave ranges per head from a rounded-down share
+                                            (12, 3, 128, W.BF16), (40, 5, 64, W.BF16)])
 def test_balanced_groups_dims_and_dtypes(Hq, Hkv, d, dtype):
     rng = np.random.default_rng(64 + Hq + Hkv + d)
     lens = np.concatenate([rng.integers(1, 3000, size=40), [16, 17, 1, 4096]])
