@@ -47,7 +47,10 @@ __global__ void __launch_bounds__(kThreads) append_kernel(AppendArgs a) {
   const int o = a.q_offsets[r];
   const int n = L - o;
   const int i0 = t * kRowsPerWg;
-  if (n <= 0 || i0 >= n) return;
+  // a negative offset would put rows at negative positions, i.e. before the
+  // request's first page: such a request is skipped, like a page id outside
+  // the pool, so no metadata can make this kernel write outside the pool
+  if (o < 0 || n <= 0 || i0 >= n) return;
   const int rows = n - i0 < kRowsPerWg ? n - i0 : kRowsPerWg;
   const int start = row_start_of(a, r);
 

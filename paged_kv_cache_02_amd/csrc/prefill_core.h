@@ -30,10 +30,17 @@
 //   * causal mask by select on diagonal tiles only; lazy online-softmax
 //     rescale (only when the max grows by more than 2^8); the row max and
 //     sum cross the two lane halves with permlane32_swap;
-//   * P is rounded to bf16 and O^T += V^T P^T: the V^T operand comes from
-//     V's natural [key][dim] layout through ds_read_b64_tr_b16 (gfx950's
-//     transposing LDS read), in the key order the P^T registers carry, and
-//     the output accumulator keeps one row per lane, so rescaling is local.
+//   * O^T += V^T P^T runs on fp16 MFMA: once a wave's copy of its V page
+//     has landed, the wave converts that page in LDS from bf16 to fp16
+//     (exact for |v| up to fp16's 65504; smaller than 2^-14 it keeps an
+//     absolute error under 2^-25), and P is rounded to fp16, whose 11-bit
+//     significand keeps each weight within 2^-12 of its fp32 value (a bf16
+//     P, 8 bits, moved outputs of rows dominated by a few keys with |v|
+//     near 4 by up to 0.009, most of the 1e-2 bar).  The V^T operand comes
+//     from V's natural [key][dim] layout through ds_read_b64_tr_b16
+//     (gfx950's transposing LDS read), in the key order the P^T registers
+//     carry, and the output accumulator keeps one row per lane, so
+//     rescaling is local.
 //
 // Keys at or past a row's position are masked by select before the max.  K
 // and V rows of keys at or past seq_len (page tails, possibly NaN) are never
@@ -66,6 +73,8 @@ constexpr int kSchedMfma = 0x0008;
 constexpr int kSchedDsRead = 0x0100;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 halfx8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 halfx2_t __attribute__((ext_vector_type(2)));
 typedef short shortx4_t __attribute__((ext_vector_type(4)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -105,6 +114,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
+__device__ __forceinline__ halfx8_t as_halfx8(const uint4& u) { return __builtin_bit_cast(halfx8_t, u); }
+
+// Two fp32 values rounded to nearest-even fp16, packed (v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  halfx2_t v;
+  v[0] = (_Float16)lo;
+  v[1] = (_Float16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// A packed bf16 pair as a packed fp16 pair (exact within fp16's range).
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t u) {
+  return pack_f16x2(__uint_as_float(u << 16), __uint_as_float(u & 0xFFFF0000u));
+}
 
 // Max and sum of x over lanes l and l ^ 32, without an LDS round trip:
 // permlane32_swap with both operands x returns x of this lane in one result
@@ -242,6 +265,27 @@ __device__ __forceinline__ void dma_tile(unsigned char* kst, unsigned char* vst,
       *reinterpret_cast<uint4*>(kst + (wave * kPerWave + i) * 1024 + lane * 16) = kv;
       *reinterpret_cast<uint4*>(vst + (wave * kPerWave + i) * 1024 + lane * 16) = vv;
     }
+  }
+}
+
+// Convert the V page this wave copied into stage `vst` (dma_tile's pieces
+// wave * kPerWave .. +kPerWave-1) from bf16 to fp16 in place.  Called after
+// the wave's copies have landed (s_waitcnt) and before the barrier that
+// hands the stage to the group; each lane rewrites only the 16 bytes it
+// reads.
+template <int D>
+__device__ __forceinline__ void v_page_to_f16(unsigned char* vst, int wave, int lane) {
+  using GE = Geo<D>;
+  constexpr int kPerWave = GE::kDmaPerTile / kWavesPerGroup;
+#pragma unroll
+  for (int i = 0; i < kPerWave; ++i) {
+    uint4* p = reinterpret_cast<uint4*>(vst + (wave * kPerWave + i) * 1024 + lane * 16);
+    uint4 x = *p;
+    x.x = bf16x2_to_f16x2(x.x);
+    x.y = bf16x2_to_f16x2(x.y);
+    x.z = bf16x2_to_f16x2(x.z);
+    x.w = bf16x2_to_f16x2(x.w);
+    *p = x;
   }
 }
 
@@ -452,9 +496,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
       // a row with no visible key so far keeps m = -inf: use 0 as the
       // reference so its (all -inf) scores give p = 0 rather than NaN
       const float mref = m_run[rb] == -INFINITY ? 0.f : m_run[rb];
-      // the row sum adds the fp32 weights (a sum of their bf16 roundings
-      // would be off by up to 2^-9 relative in a row with one dominant key,
-      // about 2e-3 in the log-sum-exp)
+      // the row sum adds the fp32 weights (a sum of their fp16 roundings
+      // would be off by up to 2^-12 relative in a row with one dominant
+      // key)
       float lsum = 0.f;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
@@ -463,7 +507,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
           const float p0 = fast_exp2(fmaf(sacc[rb][kb2][i], sl2, -mref));
           const float p1 = fast_exp2(fmaf(sacc[rb][kb2][i + 1], sl2, -mref));
           lsum += p0 + p1;
-          pk[rb][kb2][i / 2] = pack_bf16x2(p0, p1);
+          pk[rb][kb2][i / 2] = pack_f16x2(p0, p1);
         }
       }
       l_run[rb] += lsum;
@@ -500,8 +544,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
       pb.w = pk[0][kb2][4 * th + 3];
 #pragma unroll
       for (int db = 0; db < GE::kDimBlocks; ++db)
-        oacc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(avs[ks & 1][db]),
-                                                              as_bf16x8(pb), oacc[0][db], 0, 0, 0);
+        oacc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_halfx8(avs[ks & 1][db]),
+                                                             as_halfx8(pb), oacc[0][db], 0, 0, 0);
     }
     // schedule: k-step 0's reads, then each k-step's MFMAs interleaved with
     // the next k-step's reads (two per MFMA), then the last MFMAs
@@ -539,6 +583,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
     if (my0 < my1) dma_tile<D>(ks0, vs0, kpool, vpool, wave_page(my0), my0, L, Hkv, g, wave, lane);
     int next_id = wave_page(my0 + 1);
     __builtin_amdgcn_s_waitcnt(0);
+    if (my0 < my1) v_page_to_f16<D>(vs0, wave, lane);
     __syncthreads();
     for (int i = 0;;) {
       int kt = my0 + i;
@@ -546,6 +591,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
       next_id = wave_page(kt + 2);
       if (kt < my1) compute_tile(ks0, vs0, kt * kTileKeys);
       __builtin_amdgcn_s_waitcnt(0);
+      if (kt + 1 < my1) v_page_to_f16<D>(vs1, wave, lane);
       __syncthreads();
       if (++i >= nloop) break;
       kt = my0 + i;
@@ -553,6 +599,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
       next_id = wave_page(kt + 2);
       if (kt < my1) compute_tile(ks1, vs1, kt * kTileKeys);
       __builtin_amdgcn_s_waitcnt(0);
+      if (kt + 1 < my1) v_page_to_f16<D>(vs0, wave, lane);
       __syncthreads();
       if (++i >= nloop) break;
     }

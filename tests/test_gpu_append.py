@@ -76,6 +76,32 @@ def test_append_skips_rows_whose_page_is_out_of_range():
     assert np.array_equal(raw(dev["v_pool"]).view(np.uint8), ev[:-1].view(np.uint8))
 
 
+def test_append_skips_a_request_with_a_negative_offset():
+    # a negative q_offset breaks the contract (pa_validate_metadata reports
+    # it); the kernel must then skip that request rather than write before
+    # its first page
+    b, kn, vn = append_case(78, [40, 20], [8, 0], 2, 64, W.BF16)
+    dev = device_batch(b)
+    before_k, before_v = raw(dev["k_pool"]).copy(), raw(dev["v_pool"]).copy()
+    offs = dev["q_offsets"].clone()
+    offs[0] = -4                          # request 0 now claims 44 rows
+    rows0 = 40 + 4
+    rng = np.random.default_rng(5)
+    kn2 = np.concatenate([W.f32_to_bf16_bits(rng.standard_normal((rows0, 2, 64)).astype(np.float32)),
+                          kn[32:]])
+    vn2 = np.concatenate([W.f32_to_bf16_bits(rng.standard_normal((rows0, 2, 64)).astype(np.float32)),
+                          vn[32:]])
+    pa.pa_append_kv(to_torch(kn2, W.BF16), to_torch(vn2, W.BF16), dev["k_pool"], dev["v_pool"],
+                    dev["page_table"], dev["seq_lens"], offs, max_seq_len=b.max_seq_len,
+                    max_q_len=b.max_seq_len)   # a valid host bound the device offsets break
+    torch.cuda.synchronize()
+    # expected: request 1 appended, request 0 and everything else untouched
+    ek, ev = ORACLE.append_kv(before_k, before_v, b.page_table[1:], b.seq_lens[1:], b.q_offsets[1:],
+                              kn[32:], vn[32:])
+    assert np.array_equal(raw(dev["k_pool"]).view(np.uint8), ek.view(np.uint8))
+    assert np.array_equal(raw(dev["v_pool"]).view(np.uint8), ev.view(np.uint8))
+
+
 def test_serving_sequence_allocator_append_attention():
     """Three requests served for several steps: the host allocator reserves
     pages as sequences grow, pa_append_kv writes each step's K/V, then the

@@ -115,11 +115,17 @@ def test_long_context_split16_full_and_partials():
 
 
 def test_long_context_guard_plan():
+    # the route pa_decode takes on the long config (the page-balanced d = 64
+    # kernel and its range-table merge), compared on every row
     b = W.make_config("long_splitk_decode")
-    out, lse = run_decode(b)
-    for r in (3, 15):
-        ro, rl = oracle_run(b, requests=[r])
-        compare(b, out, lse, ro, rl, rows=[r], label=f"long context guard plan row {r}")
+    dev = device_batch(b)
+    desc = pa.make_desc(dev["q"], dev["k_pool"], dev["page_table"], dev["seq_lens"], b.max_seq_len)
+    plan = pa.pa_plan(desc)
+    print(f"case long context guard plan={plan}", flush=True)
+    assert plan["path"] == "decode_balanced"
+    out, lse = run_decode(b, dev)
+    ro, rl = oracle_run(b)
+    compare(b, out, lse, ro, rl, label="long context guard plan, all rows")
 
 
 # ----------------------------------------------------------------------------

@@ -35,6 +35,69 @@ def test_mixed_step_prefill_chunks_full():
     compare(b, out, lse, ro, rl, label="mixed-step prefill")
 
 
+@pytest.mark.parametrize("seed", [11, 12, 13, 14, 15])
+def test_mixed_step_prefill_chunks_other_seeds(seed):
+    # the mixed step's chunk shapes (512 tokens at offsets 0/512/1536/3072)
+    # drawn from five more seeds, each compared on every row at the plain bar
+    full = W.make_config("mixed_step", seed=seed)
+    b = full.subset(*full.notes["prefill_requests"], name=f"mixed prefill chunks seed {seed}")
+    print(f"case mixed_step prefill chunks seed {seed}", flush=True)
+    out, lse = run_prefill(b)
+    ro, rl = oracle_run(b)
+    compare(b, out, lse, ro, rl, label=f"mixed-step prefill seed {seed}")
+
+
+def few_dominant_keys_batch(seed):
+    """A 512-token chunk at offset 0 whose rows are dominated by a few keys:
+    scores x4, the V rows of the first 32 keys pushed to |v| in [3, 3.875],
+    every V clipped to |v| <= 3.875.  Early rows then average a handful of
+    large values, which is where the precision of the weights in the P V
+    product shows.  |out| stays below 4, the range where a bf16 output step
+    (2^-7 at most) leaves room under the 1e-2 bar."""
+    b = chunk_batch(seed, [512], [0], 32, 8, 128)
+    b.q = W.f32_to_bf16_bits(b.q_f32() * 4.0)
+    vp = b.v_pool_f32().copy()
+    for pg in b.page_table[0, :2]:
+        x = vp[pg]
+        vp[pg] = np.sign(x) * (3.0 + 0.875 * np.abs(np.tanh(x)))
+    b.v_pool = W.f32_to_bf16_bits(np.clip(vp, -3.875, 3.875))
+    return b
+
+
+@pytest.mark.parametrize("seed", [100, 101, 102])
+def test_rows_dominated_by_few_large_values(seed):
+    b = few_dominant_keys_batch(seed)
+    print(f"case few dominant keys seed {seed}", flush=True)
+    out, lse = run_prefill(b)
+    ro, rl = oracle_run(b)
+    st = compare(b, out, lse, ro, rl, label=f"prefill few dominant keys seed {seed}")
+    assert st["max_abs_oracle_out"] < 4.0
+
+
+def test_values_near_the_fp16_range():
+    # the P V product runs on fp16 operands: V of magnitude up to 6e4 (below
+    # fp16's 65504) must come through finite and as precise, relative to the
+    # size of V, as unit-scale V is: the error is held to 2^-8 of max |v|
+    # (an output in [2^15, 2^16) rounds to a multiple of 256, up to 2^-8.9 of
+    # 6e4, and the rest is a small share of that).  An output near zero is
+    # a cancellation of large values, so its error is measured against the
+    # scale of V, not against itself.
+    b = chunk_batch(59, [300, 130], [0, 64], 32, 8, 128)
+    vp = b.v_pool_f32().copy()
+    vp = np.sign(vp) * np.minimum(np.abs(vp) * 2.0e4, 6.0e4)
+    b.v_pool = W.f32_to_bf16_bits(vp)
+    vmax = float(np.nanmax(np.abs(b.v_pool_f32())))
+    out, lse = run_prefill(b)
+    ro, rl = oracle_run(b)
+    o = out_to_f64(out)
+    assert np.all(np.isfinite(o))
+    err = np.abs(o - ro).max() / vmax
+    print(f"[fp16 range] max |d out| / max |v| = {err:.3e}, max |v| = {vmax:.0f}", flush=True)
+    assert 50000.0 < vmax < 65504.0
+    assert err <= 2.0 ** -8
+    assert np.max(np.abs(lse.cpu().numpy() - rl)) <= LSE_TOL
+
+
 @pytest.mark.parametrize("Hq,Hkv,d", [(32, 8, 128), (16, 8, 128), (8, 8, 128), (64, 8, 128),
                                       (32, 8, 64), (4, 4, 64), (16, 1, 64)])
 def test_ragged_chunks(Hq, Hkv, d):
