@@ -17,7 +17,9 @@
  * ---------------------------------------
  *  - All array arguments are DEVICE pointers owned by the caller.  The library
  *    never allocates or frees device memory and never synchronizes (except
- *    pa_validate_metadata, which is a debugging aid).  All work is enqueued on
+ *    pa_validate_metadata, which is a debugging aid); the one piece of device
+ *    memory it holds is the fixed scratch array of pa_decode_noalloc, which
+ *    each device gets when the library is loaded.  All work is enqueued on
  *    `stream` (a hipStream_t; NULL = the null stream) and the call returns as
  *    soon as it is enqueued.
  *  - Errors are return codes; nothing aborts or throws across the ABI.
@@ -139,6 +141,25 @@ pa_status pa_decode(const pa_desc* desc, const void* q, const void* k_pool, cons
                     const int32_t* page_table, const int32_t* seq_lens, const int32_t* q_offsets,
                     float scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
                     void* stream);
+
+/* pa_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same routes, kernels and results as pa_decode, with no workspace
+ * argument.  The routes that need scratch use a fixed array of
+ * PA_NOALLOC_SCRATCH_BYTES bytes of device memory that the library holds on
+ * each device it runs on until the process ends; no call allocates or frees
+ * anything.  A call whose plan needs more scratch than that (pa_plan's
+ * workspace_bytes; for example more than about 900 requests at 64 query
+ * heads and d = 128) returns PA_ERR_WORKSPACE and does nothing.  Every call
+ * on one device shares that device's array, so calls that overlap on one
+ * device (on different streams, or from different threads without ordering)
+ * race and their results are undefined; calls ordered on one stream are
+ * safe.  Argument errors as for pa_decode. */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+pa_status pa_decode_noalloc(const pa_desc* desc, const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* page_table, const int32_t* seq_lens,
+                            const int32_t* q_offsets, float scale, void* out, float* lse,
+                            void* stream);
 
 /* Split-K decode with a caller-chosen partition count (Flash-Decoding):
  * request r's ceil(seq_lens[r]/P) pages are cut into num_splits page-aligned

@@ -53,6 +53,7 @@ _SIGS = {
     "pa_plan": (ctypes.c_int, [_D, ctypes.c_int32, ctypes.POINTER(pa_plan_info)]),
     "pa_decode": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P,
                                  ctypes.c_size_t, _P]),
+    "pa_decode_noalloc": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P]),
     "pa_split_merge": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_int32,
                                       _P, ctypes.c_size_t, _P, _P, _P]),
     "pa_prefill_chunk": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P,
@@ -177,6 +178,21 @@ def _alloc_out(q, out, lse, want_lse=True):
         out = torch.empty_like(q)
     if lse is None and want_lse:
         lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=q.device)
+    return out, lse
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def pa_decode_noalloc(q, k_pool, v_pool, page_table, seq_lens, q_offsets, scale, *, out, lse,
+                      max_seq_len=None, desc=None):
+    """pa_decode on the library's fixed device scratch: the C call allocates
+    nothing (out and lse are the caller's)."""
+    desc = desc or make_desc(q, k_pool, page_table, seq_lens, max_seq_len)
+    _check(lib().pa_decode_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                   _ptr(page_table), _ptr(seq_lens), _ptr(q_offsets),
+                                   float(scale), _ptr(out), _ptr(lse), _stream(q.device)),
+           "pa_decode_noalloc")
     return out, lse
 
 

@@ -88,7 +88,10 @@ int device_cu_count() {
   return n;
 }
 
-// Checks shared by the three decode-row entry points.
+}  // namespace
+
+namespace pa {
+// Checks shared by the decode-row entry points (declared in pa_internal.h).
 pa_status check_decode_call(const pa_desc* d, const void* q, const void* k_pool, const void* v_pool,
                             const int32_t* page_table, const int32_t* seq_lens, float scale,
                             const void* out, const float* lse) {
@@ -105,6 +108,10 @@ pa_status check_decode_call(const pa_desc* d, const void* q, const void* k_pool,
   if (!(scale > 0.f) || !isfinite(scale)) return PA_ERR_ARG;
   return PA_OK;
 }
+}  // namespace pa
+
+namespace {
+using pa::check_decode_call;
 
 size_t partial_o_bytes(const pa_desc* d, int S) {
   return align_up((size_t)d->num_seqs * d->num_q_heads * (size_t)S * d->head_dim * sizeof(float));

@@ -8,7 +8,16 @@
 
 #include <hip/hip_runtime.h>
 
+#include "pa.h"
+
 namespace pa {
+
+// Argument checks of the decode-row entry points (pa_decode and its
+// variants): the descriptor, one row per request, the head ratio, pointers,
+// alignment and scale.  Returns PA_OK or the status the entry point returns.
+pa_status check_decode_call(const pa_desc* d, const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* page_table, const int32_t* seq_lens, float scale,
+                            const void* out, const float* lse);
 
 constexpr int kPageSize = 16;  // keys per page (the only page size built)
 // Requests the page-balanced decode handles in one call (its per-request page
