@@ -44,6 +44,12 @@
  *    (position q_offsets[r] + i) sees keys 0 .. q_offsets[r] + i (causal).
  *    Query head h reads KV head h / (Hq / Hkv).  Logical key j of request r is
  *    slot j % P of physical page page_table[r][j / P].
+ *  - Head ratio G = Hq / Hkv (Hkv must divide Hq): pa_prefill_chunk takes any
+ *    G; the decode entry points take G <= 16 for bf16 and G <= 8 for fp32
+ *    (a G that is not a power of two runs the kernel built for the next
+ *    one, with the extra heads masked); pa_mixed_attention and
+ *    pa_decode_direct take G in {1, 2, 4, 8}.  Other ratios return
+ *    PA_ERR_UNSUPPORTED.
  *  - Device-array contract (checked only by pa_validate_metadata):
  *    1 <= seq_lens[r] <= max_pages_per_seq * P, 0 <= q_offsets[r] < seq_lens[r],
  *    sum_r n_r == total_q, and the first ceil(seq_lens[r] / P) entries of
@@ -125,12 +131,23 @@ typedef struct pa_plan_info {
  * cu_count <= 0 means "ask the current device" (falls back to 256). */
 pa_status pa_plan(const pa_desc* desc, int32_t cu_count, pa_plan_info* plan);
 
-/* Scratch bytes for split-K with num_splits partitions:
+/* Scratch bytes for split-K with num_splits partitions (the split-K
+ * partition of long-sequence decode: "mini-vllm-tutorial advanced-series
+ * design", section 4, Phase B, adv04 Flash-Decoding):
  * B*Hq*S*d float32 partial outputs + B*Hq*S float32 partial lse, each
  * 256-byte aligned.  Returns 0 for an invalid desc or num_splits < 1. */
 size_t pa_workspace_bytes(const pa_desc* desc, int32_t num_splits);
 
-/* Single-token decode: every request has exactly one query row (n_r = 1, so
+/* Single-token decode read straight out of the paged cache: the attention
+ * kernel walks the request's page table instead of a contiguous K/V copy,
+ * with paging and online softmax in one kernel so no score row is stored
+ * ("tiny-llm source reading", section "Paged KV Cache", the Paged
+ * FlashAttention step; "Build a vLLM from Scratch", Week 3, Direct Paged
+ * Attention + Paged FlashAttention).  It is the one-token step that the KV
+ * cache leaves after prefill ("tiny-llm source reading", section "KV Cache
+ * changes the shape of the computation"), grouped-query heads sharing each
+ * K/V load (the same page's week-one GQA item).
+ * Every request has exactly one query row (n_r = 1, so
  * total_q == B and q_offsets[r] == seq_lens[r] - 1; q_offsets may be NULL).
  * out [B, Hq, d] (dtype), lse float32 [B, Hq] (may be NULL).  The guard may
  * route through a split-K path, which needs `workspace` of at least
@@ -161,7 +178,9 @@ pa_status pa_decode_noalloc(const pa_desc* desc, const void* q, const void* k_po
                             const int32_t* q_offsets, float scale, void* out, float* lse,
                             void* stream);
 
-/* Split-K decode with a caller-chosen partition count (Flash-Decoding):
+/* Split-K decode with a caller-chosen partition count ("mini-vllm-tutorial
+ * advanced-series design", section 4, Phase B, adv04 Flash-Decoding: a long
+ * context is cut into partitions whose partial results are combined):
  * request r's ceil(seq_lens[r]/P) pages are cut into num_splits page-aligned
  * ranges of ceil(pages_r / num_splits) pages (trailing ranges may be empty).
  * Each (request, KV head, split) workgroup writes a normalized partial output
@@ -177,8 +196,8 @@ pa_status pa_split_merge(const pa_desc* desc, const void* q, const void* k_pool,
                          void* stream);
 
 /* Baselines for measuring what paging and online softmax cost (same row
- * contract and outputs as pa_decode; bf16 or fp32, d = 64 or 128, G in
- * {1, 2, 4, 8}):
+ * contract and outputs as pa_decode; bf16 or fp32, d = 64 or 128; G as for
+ * pa_decode, except pa_decode_direct: G in {1, 2, 4, 8}):
  *   pa_decode_dense:  the same fused (online-softmax) per-(request, KV head)
  *                     kernel over a dense cache k_cache, v_cache
  *                     [B, Hkv, MP * P, d] (MP = desc->max_pages_per_seq, the
@@ -200,7 +219,12 @@ pa_status pa_decode_direct(const pa_desc* desc, const void* q, const void* k_poo
                            const int32_t* page_table, const int32_t* seq_lens, float scale, void* out,
                            float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Chunked prefill: request r's n_r query rows (a chunk of a prompt at prior
+/* Chunked prefill ("tiny-llm source reading", section "Chunked Prefill": a
+ * long prompt is cut into bounded chunks that interleave with decode;
+ * "Build a vLLM from Scratch", Week 3, Chunked Prefill, on the tiled
+ * prefill attention of its Week 2; the matrix-shaped prefill kernel of the
+ * tiny-llm source reading's "Prefill and decode need different kernels"):
+ * request r's n_r query rows (a chunk of a prompt at prior
  * offset q_offsets[r]) attend causally to keys 0 .. q_offsets[r] + i, all of
  * them read from the pages (the chunk's own K/V already appended).  bf16
  * only.  q_starts: int32 [B+1] exclusive prefix sum of n_r, or NULL to derive
@@ -308,14 +332,16 @@ pa_status pa_pool_cow(pa_page_pool* pool, int32_t* page_table_row, int32_t max_p
 
 /* Copy whole pages, K and V for every KV head, from src_ids[i] to
  * dst_ids[i] (device int32 arrays of n ids; bit-exact): the device half of
- * pa_pool_cow.  A pair naming a page outside [0, num_pages), or the same
+ * pa_pool_cow, the private copy a holder of a shared page takes before
+ * writing ("mini-vllm-tutorial advanced-series design", Phase C, adv05).  A pair naming a page outside [0, num_pages), or the same
  * page twice, is skipped.  The dst pages must be distinct and none of them a
  * src page of the same call. */
 pa_status pa_copy_pages(const pa_desc* desc, void* k_pool, void* v_pool, const int32_t* src_ids,
                         const int32_t* dst_ids, int32_t n, void* stream);
 
-/* Log-sum-exp merge of split partials (the merge pass on its own; a test
- * hook).  o_part float32 [rows, heads, S, d], lse_part float32 [rows, heads, S]
+/* Log-sum-exp merge of split partials (the combine step of split-K decode,
+ * "mini-vllm-tutorial advanced-series design", section 4, Phase B, adv04;
+ * the merge pass on its own, a test hook).  o_part float32 [rows, heads, S, d], lse_part float32 [rows, heads, S]
  * (-inf marks an empty split) -> out [rows, heads, d] of out_dtype and
  * lse float32 [rows, heads] (may be NULL). */
 pa_status pa_merge_partials(int32_t rows, int32_t heads, int32_t num_splits, int32_t head_dim,
@@ -324,13 +350,17 @@ pa_status pa_merge_partials(int32_t rows, int32_t heads, int32_t num_splits, int
 
 /* Copy request `req`'s first seq_len keys out of the pools into contiguous
  * k_out, v_out [seq_len, Hkv, d] (bit-exact; the page-table translation on
- * its own, a test hook).  seq_len is a host value. */
+ * its own, a test hook).  This is the concatenation the attention kernels
+ * avoid by reading pages through the table ("tiny-llm source reading",
+ * section "Paged KV Cache").  seq_len is a host value. */
 pa_status pa_gather_kv(const pa_desc* desc, const void* k_pool, const void* v_pool,
                        const int32_t* page_table, int32_t req, int32_t seq_len, void* k_out,
                        void* v_out, void* stream);
 
 /* Debugging aid: copies the metadata to the host (synchronizing `stream`)
- * and checks the device-array contract above.  q_offsets may be NULL
+ * and checks the device-array contract above (the page table, context
+ * lengths and offsets of the "Paged KV Cache" section of the tiny-llm
+ * source reading).  q_offsets may be NULL
  * (decode).  Returns PA_OK or PA_ERR_METADATA. */
 pa_status pa_validate_metadata(const pa_desc* desc, const int32_t* page_table,
                                const int32_t* seq_lens, const int32_t* q_offsets, void* stream);

@@ -98,7 +98,7 @@ pa_status check_decode_call(const pa_desc* d, const void* q, const void* k_pool,
   pa_status st = check_desc(d);
   if (st != PA_OK) return st;
   if (d->total_q != d->num_seqs || d->max_q_len > 1) return PA_ERR_ARG;
-  if (!pa::decode_group_supported(d->num_q_heads / d->num_kv_heads)) return PA_ERR_UNSUPPORTED;
+  if (!pa::decode_group_supported(d->num_q_heads / d->num_kv_heads, d->dtype)) return PA_ERR_UNSUPPORTED;
   if (d->num_seqs == 0) return PA_OK;
   if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !out) return PA_ERR_ARG;
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out) ||
@@ -301,7 +301,7 @@ pa_status pa_plan(const pa_desc* d, int32_t cu_count, pa_plan_info* plan) {
     plan->workspace_bytes = pp.splits > 1 ? prefill_workspace_bytes(d, pp) : 0;
     return PA_OK;
   }
-  if (!pa::decode_group_supported(G)) return PA_ERR_UNSUPPORTED;
+  if (!pa::decode_group_supported(G, d->dtype)) return PA_ERR_UNSUPPORTED;
   const long long units = (long long)d->num_seqs * d->num_kv_heads;
   const int max_pages = (d->max_seq_len + d->page_size - 1) / d->page_size;
   const int V = balanced_ranges(d, cus);
@@ -382,6 +382,8 @@ pa_status pa_decode_direct(const pa_desc* d, const void* q, const void* k_pool, 
                            float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   pa_status st = check_decode_call(d, q, k_pool, v_pool, page_table, seq_lens, scale, out, lse);
   if (st != PA_OK || d->num_seqs == 0) return st;
+  const int Gd = d->num_q_heads / d->num_kv_heads;
+  if (!(Gd == 1 || Gd == 2 || Gd == 4 || Gd == 8)) return PA_ERR_UNSUPPORTED;
   if (workspace == nullptr || workspace_bytes < pa_direct_workspace_bytes(d) || !aligned16(workspace))
     return PA_ERR_WORKSPACE;
   pa::DirectArgs a;
@@ -431,8 +433,7 @@ pa_status pa_prefill_chunk(const pa_desc* d, const void* q, const void* k_pool,
   pa_status st = check_desc(d);
   if (st != PA_OK) return st;
   if (d->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
-  const int G = d->num_q_heads / d->num_kv_heads;
-  if (G < 1 || G > 16 || (G & (G - 1)) != 0) return PA_ERR_UNSUPPORTED;
+  const int G = d->num_q_heads / d->num_kv_heads;   // any ratio: rows pack (token, head) pairs
   if (d->num_seqs == 0 || d->total_q == 0) return PA_OK;
   if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !q_offsets || !out) return PA_ERR_ARG;
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out) ||
@@ -489,7 +490,7 @@ pa_status pa_mixed_attention(const pa_desc* d, const void* q, const void* k_pool
   if (st != PA_OK) return st;
   if (d->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
   const int G = d->num_q_heads / d->num_kv_heads;
-  if (!pa::decode_group_supported(G)) return PA_ERR_UNSUPPORTED;
+  if (!(G == 1 || G == 2 || G == 4 || G == 8)) return PA_ERR_UNSUPPORTED;
   if (d->num_seqs > pa::kMaxMixedSeqs) return PA_ERR_UNSUPPORTED;
   if (d->num_seqs == 0 || d->total_q == 0) return PA_OK;
   if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !q_offsets || !out) return PA_ERR_ARG;

@@ -204,10 +204,11 @@ decode_balanced_kernel(DecodeArgs a, const int32_t* __restrict__ page_table,
   int rc = lo, jc = f0 - uniform(pre[lo]), nc = npages(lo);
   int Lc = seq_len(rc);
 
+  const int Gr = Hq / Hkv;   // real group size (G: the padded one the registers hold)
   uint4 qv[G][S::kChunksPerLane], qn[G][S::kChunksPerLane];
-  load_q<T, D, G>(qv, qp, Hq, rc, g, true, col);
+  load_q<T, D, G>(qv, qp, Hq, rc, g, Gr, true, col);
   int rq = next_req(rc);  // request whose q sits in qn
-  load_q<T, D, G>(qn, qp, Hq, rq < B ? rq : B - 1, g, rq < B && uniform(pre[rq]) < f0 + nw, col);
+  load_q<T, D, G>(qn, qp, Hq, rq < B ? rq : B - 1, g, Gr, rq < B && uniform(pre[rq]) < f0 + nw, col);
 
   WaveState<T, D, G> st;
   reset_state<T, D, G>(st);
@@ -248,7 +249,8 @@ decode_balanced_kernel(DecodeArgs a, const int32_t* __restrict__ page_table,
           const size_t slot = (size_t)rc + v;
 #pragma unroll
           for (int h = 0; h < G; ++h) {
-            const int hq = g * G + h;
+            if (h >= Gr) break;
+            const int hq = g * Gr + h;
             const float l = st.l[h];
             const bool empty = !(l > 0.f);
             const float inv = empty ? 0.f : 1.f / l;
@@ -289,7 +291,7 @@ decode_balanced_kernel(DecodeArgs a, const int32_t* __restrict__ page_table,
           }
         }
         rq = next_req(rc);
-        load_q<T, D, G>(qn, qp, Hq, rq < B ? rq : B - 1, g, rq < B && uniform(pre[rq]) < f0 + nw,
+        load_q<T, D, G>(qn, qp, Hq, rq < B ? rq : B - 1, g, Gr, rq < B && uniform(pre[rq]) < f0 + nw,
                         col);
       } else {
         ++jc;
@@ -414,10 +416,11 @@ decode_mfma_kernel(DecodeArgs a, const int32_t* __restrict__ page_table,
   int rc = lo, jc = f0 - uniform(pre[lo]), nc = npages(lo);
   int Lc = seq_len(rc);
 
+  const int Gr = Hq / Hkv;   // real group size, at most the G the kernel is built for
   uint4 qv[M::kKSteps], qn[M::kKSteps];
-  load_qt<D, G>(qv, qp, Hq, rc, g, true, lane);
+  load_qt<D>(qv, qp, Hq, rc, g, Gr, true, lane);
   int rq = next_req(rc);
-  load_qt<D, G>(qn, qp, Hq, rq < B ? rq : B - 1, g, rq < B && uniform(pre[rq]) < f0 + nw, lane);
+  load_qt<D>(qn, qp, Hq, rq < B ? rq : B - 1, g, Gr, rq < B && uniform(pre[rq]) < f0 + nw, lane);
 
   MState<D> st;
   mreset<D>(st);
@@ -444,7 +447,7 @@ decode_mfma_kernel(DecodeArgs a, const int32_t* __restrict__ page_table,
       if (ahead + 1 < nw) advance_load();
       next_phys = load_id();
       const int live = Lc - jc * kPageSize;
-      page_mfma<D, G>(bufs[u], qv, st, live, a.scale_log2, vslot, lane);
+      page_mfma<D, G>(bufs[u], qv, st, live, a.scale_log2, vslot, lane, Gr);
 
       const bool range_end = i + 1 >= nw;
       if (jc + 1 >= nc || range_end) {
@@ -458,15 +461,15 @@ decode_mfma_kernel(DecodeArgs a, const int32_t* __restrict__ page_table,
           const float l = __shfl(lh, hh);
           const bool empty = !(l > 0.f);
           const float inv = empty ? 0.f : 1.f / l;
-          if (hh < G) {
-            float* o = o_part + (slot * Hq + (size_t)g * G + hh) * D + (lane & 15);
+          if (hh < Gr) {
+            float* o = o_part + (slot * Hq + (size_t)g * Gr + hh) * D + (lane & 15);
 #pragma unroll
             for (int bb = 0; bb < M::kDimBlocks; ++bb) o[16 * bb] = st.o[bb][ii] * inv;
           }
         }
-        if (qg == 0 && (lane & 15) < G) {
+        if (qg == 0 && (lane & 15) < Gr) {
           const bool empty = !(lh > 0.f);
-          lse_part[slot * Hq + (size_t)g * G + (lane & 15)] = empty ? -INFINITY : (st.m + __log2f(lh)) * kLn2;
+          lse_part[slot * Hq + (size_t)g * Gr + (lane & 15)] = empty ? -INFINITY : (st.m + __log2f(lh)) * kLn2;
         }
         if (range_end) return;
         mreset<D>(st);
@@ -480,7 +483,7 @@ decode_mfma_kernel(DecodeArgs a, const int32_t* __restrict__ page_table,
           asm volatile("" : "+v"(qv[c].x), "+v"(qv[c].y), "+v"(qv[c].z), "+v"(qv[c].w)::"memory");
         }
         rq = next_req(rc);
-        load_qt<D, G>(qn, qp, Hq, rq < B ? rq : B - 1, g, rq < B && uniform(pre[rq]) < f0 + nw, lane);
+        load_qt<D>(qn, qp, Hq, rq < B ? rq : B - 1, g, Gr, rq < B && uniform(pre[rq]) < f0 + nw, lane);
       } else {
         ++jc;
       }
@@ -500,13 +503,23 @@ hipError_t launch_mfma_t(const DecodeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The kernels are built for padded group sizes 1, 2, 4, 8 (and 16 on the
+// MFMA forms); a group size in between runs the next one up, with the heads
+// past the real group masked.
+int padded_group(int group) {
+  int p = 1;
+  while (p < group) p <<= 1;
+  return p;
+}
+
 template <int D>
 hipError_t launch_mfma_g(const DecodeArgs& a, int group, hipStream_t s) {
-  switch (group) {
+  switch (padded_group(group)) {
     case 1: return launch_mfma_t<D, 1>(a, s);
     case 2: return launch_mfma_t<D, 2>(a, s);
     case 4: return launch_mfma_t<D, 4>(a, s);
     case 8: return launch_mfma_t<D, 8>(a, s);
+    case 16: return launch_mfma_t<D, 16>(a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -555,7 +568,7 @@ hipError_t launch_bal_t(const DecodeArgs& a, hipStream_t s) {
 
 template <typename T, int D>
 hipError_t launch_bal_g(const DecodeArgs& a, int group, hipStream_t s) {
-  switch (group) {
+  switch (padded_group(group)) {
     case 1: return launch_bal_t<T, D, 1>(a, s);
     case 2: return launch_bal_t<T, D, 2>(a, s);
     case 4: return launch_bal_t<T, D, 4>(a, s);
@@ -566,19 +579,24 @@ hipError_t launch_bal_g(const DecodeArgs& a, int group, hipStream_t s) {
 
 template <typename T, int D, bool kDense>
 hipError_t launch_g(const DecodeArgs& a, int group, hipStream_t s) {
-  switch (group) {
+  switch (padded_group(group)) {
     case 1: return launch_t<T, D, 1, kDense>(a, s);
     case 2: return launch_t<T, D, 2, kDense>(a, s);
     case 4: return launch_t<T, D, 4, kDense>(a, s);
     case 8: return launch_t<T, D, 8, kDense>(a, s);
+    case 16:
+      if constexpr (sizeof(T) == 2) return launch_t<T, D, 16, kDense>(a, s);
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-bool decode_group_supported(int group) {
-  return group == 1 || group == 2 || group == 4 || group == 8;
+bool decode_group_supported(int group, int dtype) {
+  // bf16 runs the MFMA page step, whose 16-column query tile holds up to 16
+  // heads; the fp32 VALU kernels are built for up to 8
+  return group >= 1 && group <= (dtype == 0 ? 16 : 8);
 }
 
 hipError_t launch_decode_balanced(const DecodeArgs& a, int dtype, int head_dim, int group,

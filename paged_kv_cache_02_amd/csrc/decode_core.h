@@ -302,13 +302,15 @@ __device__ __forceinline__ void wave_combine(WaveState<T, D, G>& st) {
 template <typename T, int D, int G>
 using QRegs = uint4[G][Shape<T, D, G>::kChunksPerLane];
 
+// G is the padded head count the registers hold; Gr <= G is the real group
+// size: heads Gr .. G-1 read zeros (the resource covers Gr heads).
 template <typename T, int D, int G>
-__device__ __forceinline__ void load_q(QRegs<T, D, G>& qv, const T* q, int Hq, int r, int g,
+__device__ __forceinline__ void load_q(QRegs<T, D, G>& qv, const T* q, int Hq, int r, int g, int Gr,
                                        bool valid, int col) {
   using S = Shape<T, D, G>;
-  const T* base = q + ((size_t)r * Hq + (size_t)g * G) * D;
+  const T* base = q + ((size_t)r * Hq + (size_t)g * Gr) * D;
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<T*>(base), (short)0, valid ? G * D * (int)sizeof(T) : 0, kBufferWord3);
+      const_cast<T*>(base), (short)0, valid ? Gr * D * (int)sizeof(T) : 0, kBufferWord3);
 #pragma unroll
   for (int h = 0; h < G; ++h) {
 #pragma unroll
@@ -412,14 +414,15 @@ __device__ __forceinline__ void mreset(MState<D>& st) {
 }
 
 // Q^T for one (row, KV head): lane j holds head j%16's dims 32c + 8(j/16)
-// .. +7; heads at or past G read zeros (the resource covers G heads).
-template <int D, int G>
+// .. +7; heads at or past the group size Gr read zeros (the resource covers
+// Gr heads).
+template <int D>
 __device__ __forceinline__ void load_qt(uint4 (&qt)[MShape<D>::kKSteps], const __bf16* q, int Hq, int row,
-                                        int g, bool valid, int lane) {
+                                        int g, int Gr, bool valid, int lane) {
   using M = MShape<D>;
-  const __bf16* base = q + ((size_t)row * Hq + (size_t)g * G) * D;
+  const __bf16* base = q + ((size_t)row * Hq + (size_t)g * Gr) * D;
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<__bf16*>(base), (short)0, valid ? G * M::kRowBytes : 0, kBufferWord3);
+      const_cast<__bf16*>(base), (short)0, valid ? Gr * M::kRowBytes : 0, kBufferWord3);
 #pragma unroll
   for (int c = 0; c < M::kKSteps; ++c) {
     const int off = (lane & 15) * M::kRowBytes + (32 * c + 8 * (lane >> 4)) * 2;
@@ -428,10 +431,12 @@ __device__ __forceinline__ void load_qt(uint4 (&qt)[MShape<D>::kKSteps], const _
   }
 }
 
+// G: the padded group size the kernel is built for (it sets how many V
+// operands are read ahead); Gr <= G: the real one (heads Gr.. are masked).
 template <int D, int G>
 __device__ __forceinline__ void page_mfma(const MBlock<D>& b, const uint4 (&qt)[MShape<D>::kKSteps],
                                           MState<D>& st, int live, float scale_log2,
-                                          unsigned char* vslot, int lane) {
+                                          unsigned char* vslot, int lane, int Gr) {
   using M = MShape<D>;
   const int qg = lane >> 4;
   const int h = lane & 15;
@@ -460,7 +465,7 @@ __device__ __forceinline__ void page_mfma(const MBlock<D>& b, const uint4 (&qt)[
   float xm = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    x[i] = (4 * qg + i < live && h < G) ? s[i] * scale_log2 : -INFINITY;
+    x[i] = (4 * qg + i < live && h < Gr) ? s[i] * scale_log2 : -INFINITY;
     xm = fmaxf(xm, x[i]);
   }
   xm = fmaxf(xm, __shfl_xor(xm, 16));
@@ -564,9 +569,11 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, int r, int qro
   const T* __restrict__ vpool = reinterpret_cast<const T*>(a.v_pool);
   const int32_t* __restrict__ ptab = kDense ? nullptr : a.page_table + (size_t)r * a.max_pages_per_seq;
 
-  // q chunks of the lane's dims for every head of the group
+  // q chunks of the lane's dims for every head of the group (G registers
+  // sets, the real group size Gr of them loaded)
+  const int Gr = Hq / Hkv;
   uint4 qv[G][S::kChunksPerLane];
-  load_q<T, D, G>(qv, qp, Hq, qrow, g, true, col);
+  load_q<T, D, G>(qv, qp, Hq, qrow, g, Gr, true, col);
 
   WaveState<T, D, G> st;
   reset_state<T, D, G>(st);
@@ -678,7 +685,7 @@ pages_done:
   if (wave < kSlots) put(wave);
   __syncthreads();
 
-  for (int idx = threadIdx.x; idx < G * D; idx += 64 * kW) {
+  for (int idx = threadIdx.x; idx < Gr * D; idx += 64 * kW) {
     const int h = idx / D;
     const int dim = idx % D;
     float Mt = -INFINITY;
@@ -692,7 +699,7 @@ pages_done:
       lt += f * sm_l[w][h];
       ot += f * sm_acc[w][h][dim];
     }
-    const int hq = g * G + h;
+    const int hq = g * Gr + h;
     const bool empty = !(lt > 0.f);
     const float o = empty ? 0.f : ot / lt;
     const float lse2 = empty ? -INFINITY : (Mt + __log2f(lt)) * kLn2;
@@ -731,8 +738,9 @@ __device__ __forceinline__ void decode_range_mfma(const DecodeArgs& a, int r, in
   const __bf16* __restrict__ vpool = reinterpret_cast<const __bf16*>(a.v_pool);
   const int32_t* __restrict__ ptab = kDense ? nullptr : a.page_table + (size_t)r * a.max_pages_per_seq;
 
+  const int Gr = Hq / Hkv;
   uint4 qt[M::kKSteps];
-  load_qt<D, G>(qt, qp, Hq, qrow, g, true, lane);
+  load_qt<D>(qt, qp, Hq, qrow, g, Gr, true, lane);
   MState<D> st;
   mreset<D>(st);
 
@@ -768,7 +776,7 @@ __device__ __forceinline__ void decode_range_mfma(const DecodeArgs& a, int r, in
         load_mblock<D>(bufs[nb], block_ptr(kpool, phys), block_ptr(vpool, phys), ahead < nw, lane);
         next_phys = page_id(ahead + 1);
         const int live = L - (first + kW * i) * kPageSize;
-        page_mfma<D, G>(bufs[u], qt, st, live, a.scale_log2, vslots[wave], lane);
+        page_mfma<D, G>(bufs[u], qt, st, live, a.scale_log2, vslots[wave], lane, Gr);
         if (++i >= nw) goto pages_done;
       }
     }
@@ -780,7 +788,7 @@ pages_done:
   __shared__ float sm_m[kW][G];
   __shared__ float sm_l[kW][G];
   __shared__ float sm_acc[kW][G][D];
-  if (lane < G) {
+  if (lane < Gr) {
     sm_m[wave][lane] = st.m;
     sm_l[wave][lane] = lh;
   }
@@ -788,13 +796,13 @@ pages_done:
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int hh = 4 * qg + i;
-    if (hh < G) {
+    if (hh < Gr) {
 #pragma unroll
       for (int bb = 0; bb < M::kDimBlocks; ++bb) sm_acc[wave][hh][16 * bb + (lane & 15)] = st.o[bb][i];
     }
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < G * D; idx += 64 * kW) {
+  for (int idx = threadIdx.x; idx < Gr * D; idx += 64 * kW) {
     const int h = idx / D;
     const int dim = idx % D;
     float Mt = -INFINITY;
@@ -808,7 +816,7 @@ pages_done:
       lt += f * sm_l[w][h];
       ot += f * sm_acc[w][h][dim];
     }
-    const int hq = g * G + h;
+    const int hq = g * Gr + h;
     const bool empty = !(lt > 0.f);
     const float o = empty ? 0.f : ot / lt;
     const float lse2 = empty ? -INFINITY : (Mt + __log2f(lt)) * kLn2;

@@ -50,8 +50,12 @@ struct DecodeArgs {
   float scale_log2;         // scale * log2(e)
 };
 
-// dtype: 0 = bf16, 1 = fp32.  Returns hipSuccess or the launch error.
-bool decode_group_supported(int group);
+// Query heads per KV head the decode kernels take: up to 16 for bf16 (the
+// MFMA page step's query tile has 16 columns), up to 8 for fp32.  A group
+// size that is not a power of two runs the kernel built for the next one,
+// with the extra heads masked.  dtype: 0 = bf16, 1 = fp32.
+bool decode_group_supported(int group, int dtype);
+// Launchers return hipSuccess or the launch error.
 // One workgroup per (request, KV head, split); bf16 runs the MFMA form of
 // the page step, fp32 the VALU form.
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int group, hipStream_t s);

@@ -105,7 +105,7 @@ int prefill_tile_rows(int head_dim) {
 int prefill_tile_keys() { return kTileKeys; }
 
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int group, hipStream_t s) {
-  if (group < 1 || group > 16) return hipErrorNotSupported;
+  if (group < 1) return hipErrorNotSupported;
   if (head_dim == 128) return launch_d<128>(a, group, s);
   if (head_dim == 64) return launch_d<64>(a, group, s);
   return hipErrorNotSupported;

@@ -212,20 +212,26 @@ __device__ __forceinline__ int tile_page(const PageIds& pi, int kt, int m) {
   return __builtin_amdgcn_readfirstlane(id);
 }
 
-// DMA one KV tile (K and V) from the pool into an LDS stage.  The 1 KB
-// pieces of a tile split evenly over the 4 waves of a group so that wave w
-// moves exactly page w of the tile; `id` is that page's physical id
-// (uniform; -1 past the pages the request holds).  Lane l of a piece fills
-// LDS slot (key, chunk) = (first key + l / kRowChunks, l % kRowChunks) with
-// the key's chunk (l % kRowChunks) ^ swz(key).  A page whose keys are all
-// below L goes by DMA; a page holding keys at or past L (or no page) is
-// written with ordinary loads of the live keys and zeros for the rest, so a
-// NaN in a page tail never reaches LDS.
+// Copy one KV tile's K from the pool into an LDS stage, and load its V into
+// registers.  The 1 KB pieces of a tile split evenly over the 4 waves of a
+// group so that wave w moves exactly page w of the tile; `id` is that
+// page's physical id (uniform; -1 past the pages the request holds).  Lane
+// l of a piece fills LDS slot (key, chunk) = (first key + l / kRowChunks,
+// l % kRowChunks) with the key's chunk (l % kRowChunks) ^ swz(key).  A page
+// whose keys are all below L goes by DMA (K) and plain loads (V); a page
+// holding keys at or past L (or no page) is loaded key by key with zeros
+// for the rest, so a NaN in a page tail never reaches LDS.  V's registers
+// are written to LDS, converted to fp16, by store_v once they have landed.
 template <int D>
-__device__ __forceinline__ void dma_tile(unsigned char* kst, unsigned char* vst,
-                                         const __bf16* __restrict__ kpool,
-                                         const __bf16* __restrict__ vpool, int id, int kt, int L,
-                                         int Hkv, int g, int wave, int lane) {
+struct VRegs {
+  uint4 c[Geo<D>::kDmaPerTile / kWavesPerGroup];
+};
+
+template <int D>
+__device__ __forceinline__ void load_tile(unsigned char* kst, VRegs<D>& vr,
+                                          const __bf16* __restrict__ kpool,
+                                          const __bf16* __restrict__ vpool, int id, int kt, int L,
+                                          int Hkv, int g, int wave, int lane) {
   using GE = Geo<D>;
   constexpr int kPerWave = GE::kDmaPerTile / kWavesPerGroup;
   static_assert(kPerWave * GE::kKeysPerDma == kPageSize, "each wave moves one page");
@@ -247,15 +253,13 @@ __device__ __forceinline__ void dma_tile(unsigned char* kst, unsigned char* vst,
   };
   if (full) {
     // the common case, decided once per page: kPerWave DMA instructions for
-    // K and as many for V, back to back
+    // K and as many register loads for V, back to back
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i)
       __builtin_amdgcn_global_load_lds(kpool + koff(i), (lds_void*)(kst + (wave * kPerWave + i) * 1024),
                                        16, 0, 0);
 #pragma unroll
-    for (int i = 0; i < kPerWave; ++i)
-      __builtin_amdgcn_global_load_lds(vpool + voff(i), (lds_void*)(vst + (wave * kPerWave + i) * 1024),
-                                       16, 0, 0);
+    for (int i = 0; i < kPerWave; ++i) vr.c[i] = *reinterpret_cast<const uint4*>(vpool + voff(i));
   } else {
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
@@ -263,29 +267,25 @@ __device__ __forceinline__ void dma_tile(unsigned char* kst, unsigned char* vst,
       if (id >= 0 && key_base + kslot(i) < L) kv = *reinterpret_cast<const uint4*>(kpool + koff(i));
       if (id >= 0 && key_base + vslot(i) < L) vv = *reinterpret_cast<const uint4*>(vpool + voff(i));
       *reinterpret_cast<uint4*>(kst + (wave * kPerWave + i) * 1024 + lane * 16) = kv;
-      *reinterpret_cast<uint4*>(vst + (wave * kPerWave + i) * 1024 + lane * 16) = vv;
+      vr.c[i] = vv;
     }
   }
 }
 
-// Convert the V page this wave copied into stage `vst` (dma_tile's pieces
-// wave * kPerWave .. +kPerWave-1) from bf16 to fp16 in place.  Called after
-// the wave's copies have landed (s_waitcnt) and before the barrier that
-// hands the stage to the group; each lane rewrites only the 16 bytes it
-// reads.
+// Write this wave's V page (loaded by load_tile) into stage `vst`, each
+// value converted from bf16 to fp16.
 template <int D>
-__device__ __forceinline__ void v_page_to_f16(unsigned char* vst, int wave, int lane) {
+__device__ __forceinline__ void store_v(unsigned char* vst, const VRegs<D>& vr, int wave, int lane) {
   using GE = Geo<D>;
   constexpr int kPerWave = GE::kDmaPerTile / kWavesPerGroup;
 #pragma unroll
   for (int i = 0; i < kPerWave; ++i) {
-    uint4* p = reinterpret_cast<uint4*>(vst + (wave * kPerWave + i) * 1024 + lane * 16);
-    uint4 x = *p;
+    uint4 x = vr.c[i];
     x.x = bf16x2_to_f16x2(x.x);
     x.y = bf16x2_to_f16x2(x.y);
     x.z = bf16x2_to_f16x2(x.z);
     x.w = bf16x2_to_f16x2(x.w);
-    *p = x;
+    *reinterpret_cast<uint4*>(vst + (wave * kPerWave + i) * 1024 + lane * 16) = x;
   }
 }
 
@@ -476,11 +476,14 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
           for (int i = 0; i < 16; ++i)
             sacc[rb][kb2][i] = kb2 * 32 + 8 * (i / 4) + (i % 4) <= lim ? sacc[rb][kb2][i] : -INFINITY;
       }
-      float tmax = -INFINITY;
+      // the row max and the row sum below reduce in four independent
+      // chains, so their dependent-issue latency is a quarter of one chain's
+      float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[rb][kb2][i]);
+        for (int i = 0; i < 16; ++i) mx[i & 3] = fmaxf(mx[i & 3], sacc[rb][kb2][i]);
+      float tmax = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
       tmax = pair_max(tmax) * sl2;   // scale > 0 commutes with max
       const bool need = tmax > m_run[rb] + kRescaleLog2;
       if (__builtin_expect(__any(need), 0)) {
@@ -499,18 +502,18 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
       // the row sum adds the fp32 weights (a sum of their fp16 roundings
       // would be off by up to 2^-12 relative in a row with one dominant
       // key)
-      float lsum = 0.f;
+      float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
           const float p0 = fast_exp2(fmaf(sacc[rb][kb2][i], sl2, -mref));
           const float p1 = fast_exp2(fmaf(sacc[rb][kb2][i + 1], sl2, -mref));
-          lsum += p0 + p1;
+          ls[(i / 2) & 3] += p0 + p1;
           pk[rb][kb2][i / 2] = pack_f16x2(p0, p1);
         }
       }
-      l_run[rb] += lsum;
+      l_run[rb] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
     }
     // ---- O^T += V^T P^T: 4 k-steps of 16 keys ----
     // V operand: two transposing 8-byte reads per (k-step, dim block), all
@@ -580,26 +583,27 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
     // The page this wave moves for the next tile is looked up one step
     // ahead (an LDS read whose latency the step's compute hides).
     auto wave_page = [&](int kt) { return tile_page(pi, min(kt, my1 - 1), wave); };
-    if (my0 < my1) dma_tile<D>(ks0, vs0, kpool, vpool, wave_page(my0), my0, L, Hkv, g, wave, lane);
+    VRegs<D> vr;
+    if (my0 < my1) load_tile<D>(ks0, vr, kpool, vpool, wave_page(my0), my0, L, Hkv, g, wave, lane);
     int next_id = wave_page(my0 + 1);
     __builtin_amdgcn_s_waitcnt(0);
-    if (my0 < my1) v_page_to_f16<D>(vs0, wave, lane);
+    if (my0 < my1) store_v<D>(vs0, vr, wave, lane);
     __syncthreads();
     for (int i = 0;;) {
       int kt = my0 + i;
-      if (kt + 1 < my1) dma_tile<D>(ks1, vs1, kpool, vpool, next_id, kt + 1, L, Hkv, g, wave, lane);
+      if (kt + 1 < my1) load_tile<D>(ks1, vr, kpool, vpool, next_id, kt + 1, L, Hkv, g, wave, lane);
       next_id = wave_page(kt + 2);
       if (kt < my1) compute_tile(ks0, vs0, kt * kTileKeys);
       __builtin_amdgcn_s_waitcnt(0);
-      if (kt + 1 < my1) v_page_to_f16<D>(vs1, wave, lane);
+      if (kt + 1 < my1) store_v<D>(vs1, vr, wave, lane);
       __syncthreads();
       if (++i >= nloop) break;
       kt = my0 + i;
-      if (kt + 1 < my1) dma_tile<D>(ks0, vs0, kpool, vpool, next_id, kt + 1, L, Hkv, g, wave, lane);
+      if (kt + 1 < my1) load_tile<D>(ks0, vr, kpool, vpool, next_id, kt + 1, L, Hkv, g, wave, lane);
       next_id = wave_page(kt + 2);
       if (kt < my1) compute_tile(ks1, vs1, kt * kTileKeys);
       __builtin_amdgcn_s_waitcnt(0);
-      if (kt + 1 < my1) v_page_to_f16<D>(vs0, wave, lane);
+      if (kt + 1 < my1) store_v<D>(vs0, vr, wave, lane);
       __syncthreads();
       if (++i >= nloop) break;
     }

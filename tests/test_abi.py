@@ -117,6 +117,30 @@ def test_plan_reports_unbuilt_shapes(bad):
     assert e.value.code == pa.PA_ERR_UNSUPPORTED
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(24, 8), (48, 8), (28, 4), (48, 4), (16, 1)])
+def test_plan_routes_any_head_ratio_up_to_16_for_bf16_decode(Hq, Hkv):
+    # G = 3, 6, 7, 12, 16: every decode route and the prefill route accept them
+    info = pa.pa_plan(desc(Hq=Hq, Hkv=Hkv), cu_count=256)
+    assert info["path"] == "decode_balanced" and info["workspace_bytes"] > 0
+    info = pa.pa_plan(desc(B=8000, Hq=Hq, Hkv=Hkv, max_seq_len=64, NP=40000), cu_count=256)
+    assert info["path"] in ("decode", "decode_split")
+    info = pa.pa_plan(desc(Hq=Hq, Hkv=Hkv, max_q_len=300, total_q=600), cu_count=256)
+    assert info["path"] == "prefill"
+
+
+def test_plan_head_ratio_limits():
+    # fp32 decode takes up to 8 query heads per KV head, bf16 up to 16;
+    # prefill takes any ratio
+    assert pa.pa_plan(desc(Hq=6, Hkv=2, dtype=pa.PA_F32), cu_count=256)["path"] == "decode_balanced"
+    assert pa.pa_plan(desc(Hq=14, Hkv=2, dtype=pa.PA_F32), cu_count=256)["path"] == "decode_balanced"
+    for bad in (desc(Hq=18, Hkv=2, dtype=pa.PA_F32), desc(Hq=34, Hkv=2), desc(Hq=32, Hkv=1)):
+        with pytest.raises(pa.PaError) as e:
+            pa.pa_plan(bad, cu_count=256)
+        assert e.value.code == pa.PA_ERR_UNSUPPORTED
+    info = pa.pa_plan(desc(Hq=32, Hkv=1, max_q_len=300, total_q=600), cu_count=256)
+    assert info["path"] == "prefill"
+
+
 def test_entry_points_reject_null_pointers_without_touching_the_device():
     L = pa.lib()
     d = desc()

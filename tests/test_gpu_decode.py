@@ -145,6 +145,36 @@ def test_gqa_groups_and_head_dims(Hq, Hkv, d):
         compare(b, out, lse, ro, rl, label=f"G={Hq // Hkv} d={d} split {S}")
 
 
+@pytest.mark.parametrize("Hq,Hkv,d", [(24, 8, 128), (48, 8, 128), (28, 4, 128), (48, 4, 128),
+                                      (24, 8, 64), (28, 4, 64), (48, 4, 64), (16, 1, 128)])
+def test_head_ratios_that_are_not_powers_of_two(Hq, Hkv, d):
+    # G = 3, 6, 7, 12 (and 16): the kernels built for the next power of two
+    # run with the heads past G masked; the page-balanced route (pa_decode)
+    # and the equal splits (pa_split_merge) are both compared with the oracle
+    lens = [1, 15, 16, 17, 33, 100, 250, 777, 1500, 2049]
+    b = ragged(400 + Hq + Hkv + d, lens, Hq, Hkv, d)
+    print(f"case gqa ratio Hq={Hq} Hkv={Hkv} d={d}", flush=True)
+    ro, rl = oracle_run(b)
+    dev = device_batch(b)
+    desc = pa.make_desc(dev["q"], dev["k_pool"], dev["page_table"], dev["seq_lens"], b.max_seq_len)
+    assert pa.pa_plan(desc)["path"] == "decode_balanced"
+    out, lse = run_decode(b, dev)
+    compare(b, out, lse, ro, rl, label=f"G={Hq // Hkv} d={d}")
+    out, lse, _ = run_split(b, 3, dev)
+    compare(b, out, lse, ro, rl, label=f"G={Hq // Hkv} d={d} split 3")
+
+
+@pytest.mark.parametrize("Hq,Hkv,d", [(6, 2, 64), (12, 2, 128), (7, 1, 64)])
+def test_fp32_head_ratios_that_are_not_powers_of_two(Hq, Hkv, d):
+    b = ragged(500 + Hq + d, [3, 16, 47, 129, 600], Hq, Hkv, d, dtype=W.F32)
+    print(f"case fp32 gqa ratio Hq={Hq} Hkv={Hkv} d={d}", flush=True)
+    ro, rl = oracle_run(b)
+    out, lse = run_decode(b)
+    compare(b, out, lse, ro, rl, label=f"fp32 G={Hq // Hkv} d={d}")
+    out, lse, _ = run_split(b, 3)
+    compare(b, out, lse, ro, rl, label=f"fp32 G={Hq // Hkv} d={d} split")
+
+
 @pytest.mark.parametrize("Hq,Hkv,d", [(4, 2, 64), (8, 2, 128), (8, 1, 64)])
 def test_fp32_shapes(Hq, Hkv, d):
     b = ragged(300 + Hq + d, [3, 16, 47, 129], Hq, Hkv, d, dtype=W.F32)

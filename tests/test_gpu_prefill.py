@@ -99,7 +99,9 @@ def test_values_near_the_fp16_range():
 
 
 @pytest.mark.parametrize("Hq,Hkv,d", [(32, 8, 128), (16, 8, 128), (8, 8, 128), (64, 8, 128),
-                                      (32, 8, 64), (4, 4, 64), (16, 1, 64)])
+                                      (32, 8, 64), (4, 4, 64), (16, 1, 64),
+                                      (24, 8, 128), (48, 8, 128), (28, 4, 128), (48, 4, 64),
+                                      (24, 1, 128)])
 def test_ragged_chunks(Hq, Hkv, d):
     # chunk lengths not multiples of the 128-row tile, offsets not page-aligned,
     # a one-token chunk, a chunk starting at 0 and a chunk spanning many pages
