@@ -91,6 +91,12 @@ int device_cu_count() {
 }  // namespace
 
 namespace pa {
+bool decode_group_supported(int group, int dtype) {
+  // bf16 runs the MFMA page step, whose 16-column query tile holds up to 16
+  // heads; the fp32 VALU kernels are built for up to 8
+  return group >= 1 && group <= (dtype == PA_BF16 ? 16 : 8);
+}
+
 // Checks shared by the decode-row entry points (declared in pa_internal.h).
 pa_status check_decode_call(const pa_desc* d, const void* q, const void* k_pool, const void* v_pool,
                             const int32_t* page_table, const int32_t* seq_lens, float scale,

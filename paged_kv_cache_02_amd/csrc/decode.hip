@@ -593,12 +593,6 @@ hipError_t launch_g(const DecodeArgs& a, int group, hipStream_t s) {
 
 }  // namespace
 
-bool decode_group_supported(int group, int dtype) {
-  // bf16 runs the MFMA page step, whose 16-column query tile holds up to 16
-  // heads; the fp32 VALU kernels are built for up to 8
-  return group >= 1 && group <= (dtype == 0 ? 16 : 8);
-}
-
 hipError_t launch_decode_balanced(const DecodeArgs& a, int dtype, int head_dim, int group,
                                   hipStream_t s) {
   if (dtype == 0) {
