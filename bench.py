@@ -312,14 +312,29 @@ def load_traffic(kernel: str, src_hash: str):
     return rec.get("bytes_per_launch")
 
 
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(full, budget_s: float):
     """The oracle, untuned, on a bounded sample of the same workload."""
     import oracle as ORACLE
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+        blas = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    affinity = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    # the oracle's matrix products run on the BLAS pool, bounded by the CPUs
+    # this process may use
+    threads = max(1, min(blas, affinity))
     q, kp, vp = full.q_f32(), full.k_pool_f32(), full.v_pool_f32()
     dec0, dec1 = full.notes["decode_requests"]
     pf0, pf1 = full.notes["prefill_requests"]
@@ -354,7 +369,8 @@ def cpu_baseline(full, budget_s: float):
         "sample": f"{done} of 60 decode rows ({nbytes / 1e6:.1f} MB of KV) in {t_dec:.1f} s; "
                   f"prefill: {rows} rows of the 512-token chunk at offset 3072 in {t_pf:.1f} s",
         "prefill_value": round(flops / t_pf / 1e12, 6), "prefill_unit": "TFLOP/s",
-        "host_cpus": os.cpu_count(),
+        "host_cpus": os.cpu_count(), "affinity_cpus": affinity, "blas_threads": blas,
+        "cpu_model": host_cpu_model(),
     }
 
 
