@@ -315,7 +315,6 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
   __shared__ __align__(1024) unsigned char k_b0[GE::kTileBytes];
   __shared__ __align__(1024) unsigned char k_b1[GE::kTileBytes];
   __shared__ int s_pages[kLdsPages];
-  __shared__ float s_ml[kWavesPerGroup][2][64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -379,12 +378,13 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
   const int p0 = kt0 * kPagesPerTile;
   const int p1 = min(kt1 * kPagesPerTile, npages);
   if (p1 - p0 <= kLdsPages) {
+    // published by the barrier after the first tile's copy, which reads its
+    // page straight from the table
     for (int i = p0 + tid; i < p1; i += kThreads) {
       int id = ptab[i];
       s_pages[i - p0] = id < 0 ? 0 : (id >= a.num_pages ? a.num_pages - 1 : id);
     }
     pi.lds = s_pages - p0;   // indexed by logical page
-    __syncthreads();
   }
 
   floatx16_t oacc[kRB][GE::kDimBlocks];
@@ -583,12 +583,14 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
     // The page this wave moves for the next tile is looked up one step
     // ahead (an LDS read whose latency the step's compute hides).
     auto wave_page = [&](int kt) { return tile_page(pi, min(kt, my1 - 1), wave); };
+    PageIds direct = pi;
+    direct.lds = nullptr;   // the first tile's page comes from the table itself
     VRegs<D> vr;
-    if (my0 < my1) load_tile<D>(ks0, vr, kpool, vpool, wave_page(my0), my0, L, Hkv, g, wave, lane);
-    int next_id = wave_page(my0 + 1);
+    if (my0 < my1) load_tile<D>(ks0, vr, kpool, vpool, tile_page(direct, my0, wave), my0, L, Hkv, g, wave, lane);
     __builtin_amdgcn_s_waitcnt(0);
     if (my0 < my1) store_v<D>(vs0, vr, wave, lane);
-    __syncthreads();
+    __syncthreads();   // stage 0 and the page ids in LDS
+    int next_id = wave_page(my0 + 1);
     for (int i = 0;;) {
       int kt = my0 + i;
       if (kt + 1 < my1) load_tile<D>(ks1, vr, kpool, vpool, next_id, kt + 1, L, Hkv, g, wave, lane);
@@ -613,91 +615,120 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
   else
     run(GroupTag<1>{});
 
-  // ---- merge the groups: group 1 hands its per-lane state to group 0 ----
+  // ---- merge the groups ----
   // Every lane of both groups owns the same (row, dims), so the merge is the
-  // log-sum-exp rule applied lane by lane.  Group 1's stage buffers are free
-  // now (the last barrier above ended all reads); wave w of the group writes
-  // its accumulator into one of them, float4 j of lane l at j*1024 + l*16.
-  {
-    unsigned char* xfer = wave == 0 ? k_b0 : (wave == 1 ? v_b0 : (wave == 2 ? k_b1 : v_b1));
-    if (grp == 1) {
+  // log-sum-exp rule applied lane by lane.  Each group keeps half of the dim
+  // blocks (group 0 the first, group 1 the second) and hands the other half
+  // to the other group through its own stage buffers, which are free now
+  // (the last barrier above ended all reads): wave w of a group writes into
+  // one buffer, float4 j of lane l at j*1024 + l*16.  Both groups then
+  // finalize and store their half, so the exchange and the output stores
+  // are shared by all eight waves.  The merged values are formed by the
+  // same expression in both groups (group 0's state first), so the row sums
+  // the two halves are normalized by are bit-identical.
+  constexpr int kHalf = GE::kDimBlocks / 2;
+  static_assert(GE::kDimBlocks % 2 == 0, "two halves of the dim blocks");
+  // the running max and sum follow the float4s in the same buffer
+  constexpr int kMlOff = kHalf * 4 * 1024;
+  static_assert(kMlOff + 2 * 64 * 4 <= GE::kTileBytes, "exchange fits a stage buffer");
+  auto finish = [&](auto gtag) __attribute__((always_inline)) {
+    constexpr int GRP = decltype(gtag)::value;
+    constexpr int kKeep = GRP == 0 ? 0 : kHalf;   // first dim block this group keeps
+    constexpr int kGive = GRP == 0 ? kHalf : 0;   // first dim block it hands over
+    unsigned char* mine = GRP == 0 ? (wave == 0 ? k_a0 : (wave == 1 ? v_a0 : (wave == 2 ? k_a1 : v_a1)))
+                                   : (wave == 0 ? k_b0 : (wave == 1 ? v_b0 : (wave == 2 ? k_b1 : v_b1)));
+    const unsigned char* theirs =
+        GRP == 1 ? (wave == 0 ? k_a0 : (wave == 1 ? v_a0 : (wave == 2 ? k_a1 : v_a1)))
+                 : (wave == 0 ? k_b0 : (wave == 1 ? v_b0 : (wave == 2 ? k_b1 : v_b1)));
 #pragma unroll
-      for (int db = 0; db < GE::kDimBlocks; ++db)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          float4 w;
-          w.x = oacc[0][db][4 * v + 0];
-          w.y = oacc[0][db][4 * v + 1];
-          w.z = oacc[0][db][4 * v + 2];
-          w.w = oacc[0][db][4 * v + 3];
-          *reinterpret_cast<float4*>(xfer + (db * 4 + v) * 1024 + lane * 16) = w;
-        }
-      s_ml[wave][0][lane] = m_run[0];
-      s_ml[wave][1][lane] = l_run[0];
-    }
-    __syncthreads();
-    if (grp == 1) return;
-    const float mB = s_ml[wave][0][lane];
-    const float lB = s_ml[wave][1][lane];
-    const float M = fmaxf(m_run[0], mB);
-    const float fA = m_run[0] == -INFINITY ? 0.f : fast_exp2(m_run[0] - M);
-    const float fB = mB == -INFINITY ? 0.f : fast_exp2(mB - M);
-#pragma unroll
-    for (int db = 0; db < GE::kDimBlocks; ++db)
+    for (int j = 0; j < kHalf; ++j)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float4 w = *reinterpret_cast<const float4*>(xfer + (db * 4 + v) * 1024 + lane * 16);
-        oacc[0][db][4 * v + 0] = oacc[0][db][4 * v + 0] * fA + w.x * fB;
-        oacc[0][db][4 * v + 1] = oacc[0][db][4 * v + 1] * fA + w.y * fB;
-        oacc[0][db][4 * v + 2] = oacc[0][db][4 * v + 2] * fA + w.z * fB;
-        oacc[0][db][4 * v + 3] = oacc[0][db][4 * v + 3] * fA + w.w * fB;
+        float4 w;
+        w.x = oacc[0][kGive + j][4 * v + 0];
+        w.y = oacc[0][kGive + j][4 * v + 1];
+        w.z = oacc[0][kGive + j][4 * v + 2];
+        w.w = oacc[0][kGive + j][4 * v + 3];
+        *reinterpret_cast<float4*>(mine + (j * 4 + v) * 1024 + lane * 16) = w;
       }
-    l_run[0] = l_run[0] * fA + lB * fB;
+    reinterpret_cast<float*>(mine + kMlOff)[lane] = m_run[0];
+    reinterpret_cast<float*>(mine + kMlOff)[64 + lane] = l_run[0];
+    __syncthreads();
+    const float mO = reinterpret_cast<const float*>(theirs + kMlOff)[lane];
+    const float lO = reinterpret_cast<const float*>(theirs + kMlOff)[64 + lane];
+    const float mA = GRP == 0 ? m_run[0] : mO;   // group 0's state
+    const float mB = GRP == 0 ? mO : m_run[0];
+    const float lA = GRP == 0 ? l_run[0] : lO;
+    const float lB = GRP == 0 ? lO : l_run[0];
+    const float M = fmaxf(mA, mB);
+    const float fA = mA == -INFINITY ? 0.f : fast_exp2(mA - M);
+    const float fB = mB == -INFINITY ? 0.f : fast_exp2(mB - M);
+#pragma unroll
+    for (int j = 0; j < kHalf; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float4 w = *reinterpret_cast<const float4*>(theirs + (j * 4 + v) * 1024 + lane * 16);
+        const float o4[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float own = oacc[0][kKeep + j][4 * v + e];
+          const float xa = GRP == 0 ? own : o4[e];
+          const float xb = GRP == 0 ? o4[e] : own;
+          oacc[0][kKeep + j][4 * v + e] = xa * fA + xb * fB;
+        }
+      }
+    l_run[0] = lA * fA + lB * fB;
     m_run[0] = M;
-  }
 
-  // ---- normalize and write: final output, or this split's partial ----
-  const bool partial = nsp > 1;
-  const size_t unit = ((size_t)r * T + t) * Hkv + g;
+    // ---- normalize and write this group's half: final output, or the split's partial
+    const bool partial = nsp > 1;
+    const size_t unit = ((size_t)r * T + t) * Hkv + g;
 #pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) {
-    const float l_tot = pair_sum(l_run[rb]);
-    if (!row_valid[rb]) continue;
-    const bool empty = !(l_tot > 0.f);
-    const float inv = empty ? 0.f : 1.f / l_tot;
-    const float lse = empty ? -INFINITY : (m_run[rb] + __log2f(l_tot)) * kLn2;
-    if (!partial) {
-      __bf16* orow = reinterpret_cast<__bf16*>(a.out) +
-                     ((size_t)(q_start + tok[rb]) * Hq + (size_t)g * group + hh[rb]) * D;
+    for (int rb = 0; rb < kRB; ++rb) {
+      const float l_tot = pair_sum(l_run[rb]);
+      if (!row_valid[rb]) continue;
+      const bool empty = !(l_tot > 0.f);
+      const float inv = empty ? 0.f : 1.f / l_tot;
+      const float lse = empty ? -INFINITY : (m_run[rb] + __log2f(l_tot)) * kLn2;
+      if (!partial) {
+        __bf16* orow = reinterpret_cast<__bf16*>(a.out) +
+                       ((size_t)(q_start + tok[rb]) * Hq + (size_t)g * group + hh[rb]) * D;
 #pragma unroll
-      for (int db = 0; db < GE::kDimBlocks; ++db)
+        for (int j = 0; j < kHalf; ++j)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          uint2 w;
-          w.x = pack_bf16x2(oacc[rb][db][4 * v + 0] * inv, oacc[rb][db][4 * v + 1] * inv);
-          w.y = pack_bf16x2(oacc[rb][db][4 * v + 2] * inv, oacc[rb][db][4 * v + 3] * inv);
-          *reinterpret_cast<uint2*>(orow + db * 32 + 8 * v + 4 * half) = w;
-        }
-      if (a.lse != nullptr && half == 0)
-        a.lse[(size_t)(q_start + tok[rb]) * Hq + (size_t)g * group + hh[rb]] = lse;
-    } else {
-      const int prow = wave * kRowsPerWave + rb * 32 + lrow;   // row within the tile
-      const size_t pidx = (unit * S + split) * kTileRows + prow;
-      float* po = a.part_o + pidx * D;
+          for (int v = 0; v < 4; ++v) {
+            const int db = kKeep + j;
+            uint2 w;
+            w.x = pack_bf16x2(oacc[rb][db][4 * v + 0] * inv, oacc[rb][db][4 * v + 1] * inv);
+            w.y = pack_bf16x2(oacc[rb][db][4 * v + 2] * inv, oacc[rb][db][4 * v + 3] * inv);
+            *reinterpret_cast<uint2*>(orow + db * 32 + 8 * v + 4 * half) = w;
+          }
+        if (GRP == 0 && a.lse != nullptr && half == 0)
+          a.lse[(size_t)(q_start + tok[rb]) * Hq + (size_t)g * group + hh[rb]] = lse;
+      } else {
+        const int prow = wave * kRowsPerWave + rb * 32 + lrow;   // row within the tile
+        const size_t pidx = (unit * S + split) * kTileRows + prow;
+        float* po = a.part_o + pidx * D;
 #pragma unroll
-      for (int db = 0; db < GE::kDimBlocks; ++db)
+        for (int j = 0; j < kHalf; ++j)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          float4 w;
-          w.x = oacc[rb][db][4 * v + 0] * inv;
-          w.y = oacc[rb][db][4 * v + 1] * inv;
-          w.z = oacc[rb][db][4 * v + 2] * inv;
-          w.w = oacc[rb][db][4 * v + 3] * inv;
-          *reinterpret_cast<float4*>(po + db * 32 + 8 * v + 4 * half) = w;
-        }
-      if (half == 0) a.part_lse[pidx] = lse;
+          for (int v = 0; v < 4; ++v) {
+            const int db = kKeep + j;
+            float4 w;
+            w.x = oacc[rb][db][4 * v + 0] * inv;
+            w.y = oacc[rb][db][4 * v + 1] * inv;
+            w.z = oacc[rb][db][4 * v + 2] * inv;
+            w.w = oacc[rb][db][4 * v + 3] * inv;
+            *reinterpret_cast<float4*>(po + db * 32 + 8 * v + 4 * half) = w;
+          }
+        if (GRP == 0 && half == 0) a.part_lse[pidx] = lse;
+      }
     }
-  }
+  };
+  if (grp == 0)
+    finish(GroupTag<0>{});
+  else
+    finish(GroupTag<1>{});
 }
 
 }  // namespace pf
