@@ -135,8 +135,6 @@ struct Half {  // the K (or V) registers of one (page, KV head) block
 
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
-// Buffer resource word 3 for gfx9-family raw (unstructured) buffers.
-constexpr int kBufferWord3 = 0x00020000;
 // Cache-policy bits of a buffer load: nontemporal (streamed past the caches).
 constexpr int kLoadNontemporal = 2;
 
@@ -489,10 +487,10 @@ __device__ __forceinline__ void page_mfma(const MBlock<D>& b, const uint4 (&qt)[
     p[i] = x[i] == -INFINITY ? 0.f : fast_exp2(x[i] - mref);
     st.l += p[i];
   }
-  // p as the sum of two bf16 parts: a single bf16 rounding (2^-9 relative)
-  // would move outputs of a few keys by up to |v| * 2^-9, which with
-  // |v| ~ 4 is a bf16 output step; with hi + lo the products keep about 16
-  // bits, and V itself is exact
+  // p as the sum of two bf16 parts: a single bf16 rounding (up to 2^-8
+  // relative) would move outputs of a few keys by up to |v| * 2^-8, which
+  // with |v| ~ 4 is a bf16 output step; with hi + lo the products keep
+  // about 16 bits, and V itself is exact
   bf16x4_t pa, pb;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {

@@ -20,6 +20,8 @@ pa_status check_decode_call(const pa_desc* d, const void* q, const void* k_pool,
                             const void* out, const float* lse);
 
 constexpr int kPageSize = 16;  // keys per page (the only page size built)
+// Buffer resource word 3 for gfx9-family raw (unstructured) buffers.
+constexpr int kBufferWord3 = 0x00020000;
 // Requests the page-balanced decode handles in one call (its per-request page
 // prefix lives in LDS).
 constexpr int kMaxBalancedSeqs = 4096;

@@ -18,26 +18,26 @@
 // and write partial results, combined by a merge pass.
 //
 // Keys stream in tiles of 64 (4 pages); per wave group and KV tile:
-//   * K and V pages are copied straight from HBM into LDS with
-//     global_load_lds (no staging registers), double-buffered one tile
-//     ahead; K's 16-byte chunks are XOR-swizzled by key and V is stored as
-//     [dim block][key] within each 1 KB piece, so the operand reads below
-//     are bank-conflict free and every V read is one register plus an
-//     immediate offset;
+//   * K pages are copied straight from HBM into LDS with global_load_lds (no
+//     staging registers), double-buffered one tile ahead, K's 16-byte chunks
+//     XOR-swizzled by key; V pages are loaded into registers at the same
+//     time and, once they have landed, converted from bf16 to fp16 and
+//     written to the other LDS stage as [dim block][key] within each 1 KB
+//     piece.  The operand reads below are bank-conflict free, and every
+//     operand address is one register plus an immediate offset;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: A = K rows read from LDS,
 //     B = Q held in registers, so a lane owns one query row and 16 of every
 //     32 keys -- the row max and sum need one exchange with lane ^ 32;
 //   * causal mask by select on diagonal tiles only; lazy online-softmax
 //     rescale (only when the max grows by more than 2^8); the row max and
 //     sum cross the two lane halves with permlane32_swap;
-//   * O^T += V^T P^T runs on fp16 MFMA: once a wave's copy of its V page
-//     has landed, the wave converts that page in LDS from bf16 to fp16
-//     (exact for |v| up to fp16's 65504; smaller than 2^-14 it keeps an
+//   * O^T += V^T P^T runs on fp16 MFMA: V converted from bf16 to fp16 is
+//     exact for |v| up to fp16's 65504 (smaller than 2^-14 it keeps an
 //     absolute error under 2^-25), and P is rounded to fp16, whose 11-bit
-//     significand keeps each weight within 2^-12 of its fp32 value (a bf16
-//     P, 8 bits, moved outputs of rows dominated by a few keys with |v|
-//     near 4 by up to 0.009, most of the 1e-2 bar).  The V^T operand comes
-//     from V's natural [key][dim] layout through ds_read_b64_tr_b16
+//     significand keeps each weight within 2^-11 (relative) of its fp32
+//     value (a bf16 P, 8 bits, moved outputs of rows dominated by a few
+//     keys with |v| near 4 by up to 0.009, most of the 1e-2 bar).  The V^T
+//     operand comes from V's natural [key][dim] layout through ds_read_b64_tr_b16
 //     (gfx950's transposing LDS read), in the key order the P^T registers
 //     carry, and the output accumulator keeps one row per lane, so
 //     rescaling is local.
@@ -78,6 +78,7 @@ typedef _Float16 halfx2_t __attribute__((ext_vector_type(2)));
 typedef short shortx4_t __attribute__((ext_vector_type(4)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 template <int D>
 struct Geo {
@@ -102,6 +103,10 @@ template <int D>
 __device__ __forceinline__ int swz(int key) {
   return D == 128 ? (((key & 3) << 2) | ((key >> 2) & 3)) : ((key >> 1) & 3);
 }
+
+// Keys whose swizzle repeats: swz<D>(key) depends on key modulo this.
+template <int D>
+constexpr int swz_period() { return D == 128 ? 16 : 8; }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -236,7 +241,11 @@ __device__ __forceinline__ void load_tile(unsigned char* kst, VRegs<D>& vr,
   constexpr int kPerWave = GE::kDmaPerTile / kWavesPerGroup;
   static_assert(kPerWave * GE::kKeysPerDma == kPageSize, "each wave moves one page");
   const int key_base = kt * kTileKeys + wave * kPageSize;   // absolute key of the page's slot 0
-  const size_t page_off = ((size_t)(id < 0 ? 0 : id) * Hkv + g) * ((size_t)kPageSize * D);
+  // the (page, KV head) block's first byte: uniform, so a page's loads take
+  // a buffer resource in scalar registers and a 32-bit lane offset
+  const size_t page_bytes = ((size_t)(id < 0 ? 0 : id) * Hkv + g) * ((size_t)kPageSize * GE::kRowBytes);
+  const unsigned char* __restrict__ kpage = reinterpret_cast<const unsigned char*>(kpool) + page_bytes;
+  const unsigned char* __restrict__ vpage = reinterpret_cast<const unsigned char*>(vpool) + page_bytes;
   const bool full = id >= 0 && key_base + kPageSize <= L;
   // lane offsets of piece i: K rows in order with their 16-byte chunks
   // XOR-swizzled by key; V as [dim block][key][4 chunks], so the transposing
@@ -245,27 +254,37 @@ __device__ __forceinline__ void load_tile(unsigned char* kst, VRegs<D>& vr,
   auto vslot = [&](int i) { return i * GE::kKeysPerDma + (lane / 4) % GE::kKeysPerDma; };
   auto koff = [&](int i) {
     const int kchunk = (lane % GE::kRowChunks) ^ swz<D>(wave * kPageSize + kslot(i));
-    return page_off + (size_t)kslot(i) * D + kchunk * 8;
+    return (uint32_t)(kslot(i) * GE::kRowBytes + kchunk * 16);
   };
   auto voff = [&](int i) {
     const int vchunk = 4 * (lane / (4 * GE::kKeysPerDma)) + (lane & 3);
-    return page_off + (size_t)vslot(i) * D + vchunk * 8;
+    return (uint32_t)(vslot(i) * GE::kRowBytes + vchunk * 16);
   };
   if (full) {
     // the common case, decided once per page: kPerWave DMA instructions for
-    // K and as many register loads for V, back to back
+    // K and as many register loads for V, back to back, through buffer
+    // resources spanning the page's block (the lane offsets are the same for
+    // every page, and piece i's part of them is an immediate offset)
+    constexpr int kBlockBytes = kPageSize * GE::kRowBytes;
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned char*>(kpage), (short)0, kBlockBytes, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned char*>(vpage), (short)0, kBlockBytes, kBufferWord3);
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i)
-      __builtin_amdgcn_global_load_lds(kpool + koff(i), (lds_void*)(kst + (wave * kPerWave + i) * 1024),
-                                       16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kst + (wave * kPerWave + i) * 1024), 16,
+                                               (int)koff(i), 0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < kPerWave; ++i) vr.c[i] = *reinterpret_cast<const uint4*>(vpool + voff(i));
+    for (int i = 0; i < kPerWave; ++i) {
+      const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)voff(i), 0, 0);
+      vr.c[i] = make_uint4(x[0], x[1], x[2], x[3]);
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
       uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-      if (id >= 0 && key_base + kslot(i) < L) kv = *reinterpret_cast<const uint4*>(kpool + koff(i));
-      if (id >= 0 && key_base + vslot(i) < L) vv = *reinterpret_cast<const uint4*>(vpool + voff(i));
+      if (id >= 0 && key_base + kslot(i) < L) kv = *reinterpret_cast<const uint4*>(kpage + koff(i));
+      if (id >= 0 && key_base + vslot(i) < L) vv = *reinterpret_cast<const uint4*>(vpage + voff(i));
       *reinterpret_cast<uint4*>(kst + (wave * kPerWave + i) * 1024 + lane * 16) = kv;
       vr.c[i] = vv;
     }
@@ -414,39 +433,52 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
   const uint32_t vlane = (uint32_t)((vkey / GE::kKeysPerDma) * 1024 + (vkey % GE::kKeysPerDma) * 64 +
                                     (vdim_off >> 3) * 16 + (vdim_off & 7) * 2);
 
+  // K operand addresses within a stage, the same for every tile: for k-step
+  // s the swizzled chunk 2s + half of key row lrow sits at kbase ^ (32 s)
+  // (the swizzle is an XOR on chunk bits 1..3, and the row base is a
+  // multiple of the row size).  The swizzle depends on the key modulo 16
+  // only, so the second key block's rows sit kKeyBlockBytes further on.
+  // The registers hold the offsets plus kKBias, the 64 KB that the V stages
+  // take before the K stages at d = 128, hidden from the compiler: a read
+  // then is one register plus an immediate offset (the stage's address
+  // minus the bias, plus the key block), instead of a register plus an
+  // address past the 16-bit offset field that needs an add per read.
+  constexpr uint32_t kKeyBlockBytes = 32 * GE::kRowBytes;
+  constexpr uint32_t kKBias = (4u * GE::kTileBytes) & ~0xFFFFu;
+  static_assert(swz_period<D>() <= 32, "key block 1 has key block 0's swizzle");
+  uint32_t kaddr[GE::kKSteps];
+  {
+    const int sw = swz<D>(lrow);
+    const uint32_t kbase = (uint32_t)(lrow * GE::kRowBytes) + ((uint32_t)(half ^ (sw & 1)) << 4) +
+                           ((uint32_t)(sw >> 1) << 5);
+#pragma unroll
+    for (int s = 0; s < GE::kKSteps; ++s) {
+      kaddr[s] = (kbase ^ (uint32_t)(s << 5)) + kKBias;
+      asm volatile("" : "+v"(kaddr[s]));
+    }
+  }
+
   // one KV tile out of an LDS stage
   auto compute_tile = [&](const unsigned char* kst, const unsigned char* vst, int kb)
                           __attribute__((always_inline)) {
     if (kb > pos_hi) return;   // no key of the tile is visible to any row of this wave
     // ---- S^T = K Q^T: 2 key blocks x 2 row blocks ----
-    // K operand address for k-step s: the swizzled chunk 2s + half of key
-    // row kb2*32 + lrow sits at kbase ^ (32 s) (the swizzle is an XOR on
-    // chunk bits 1..3, and the row base is a multiple of 256 bytes).
     // All 8 K operands of a key block are requested before its MFMAs, and
     // each register is refilled with the next block's operand as soon as its
     // MFMA has been issued, so the MFMAs never wait on one LDS round trip
     // each.
     static_assert(kRB == 1, "the operand pipeline below is written for one row block");
     floatx16_t sacc[kRB][2];
-    uint32_t kbase[2];
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      const int key = kb2 * 32 + lrow;
-      const int sw = swz<D>(key);
-      kbase[kb2] = (uint32_t)(key * GE::kRowBytes) + ((uint32_t)(half ^ (sw & 1)) << 4) +
-                   ((uint32_t)(sw >> 1) << 5);
-    }
-    asm volatile("" : "+v"(kbase[0]), "+v"(kbase[1]));   // keep the addresses out of the loop preheader
     uint4 ka[GE::kKSteps];
 #pragma unroll
     for (int s = 0; s < GE::kKSteps; ++s)
-      ka[s] = *reinterpret_cast<const uint4*>(kst + (kbase[0] ^ (uint32_t)(s << 5)));
+      ka[s] = *reinterpret_cast<const uint4*>(kst + (kaddr[s] - kKBias));
 #pragma unroll
     for (int s = 0; s < GE::kKSteps; ++s) {
       const floatx16_t zero = {};
       sacc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[s]), as_bf16x8(qv[0][s]),
                                                            s == 0 ? zero : sacc[0][0], 0, 0, 0);
-      ka[s] = *reinterpret_cast<const uint4*>(kst + (kbase[1] ^ (uint32_t)(s << 5)));
+      ka[s] = *reinterpret_cast<const uint4*>(kst + (kaddr[s] - kKBias + kKeyBlockBytes));
     }
 #pragma unroll
     for (int s = 0; s < GE::kKSteps; ++s) {
@@ -500,7 +532,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
       // reference so its (all -inf) scores give p = 0 rather than NaN
       const float mref = m_run[rb] == -INFINITY ? 0.f : m_run[rb];
       // the row sum adds the fp32 weights (a sum of their fp16 roundings
-      // would be off by up to 2^-12 relative in a row with one dominant
+      // would be off by up to 2^-11 relative in a row with one dominant
       // key)
       float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
