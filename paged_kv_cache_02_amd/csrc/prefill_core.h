@@ -204,7 +204,9 @@ struct PageIds {
   int npages, num_pages;
 };
 
-__device__ __forceinline__ int tile_page(const PageIds& pi, int kt, int m) {
+// The same value in every lane, still in a vector register: a lookahead
+// keeps it there until use, so the wait for its load falls where it is used.
+__device__ __forceinline__ int tile_page_lanes(const PageIds& pi, int kt, int m) {
   const int lp = kt * kPagesPerTile + m;
   if (lp >= pi.npages) return -1;
   int id;
@@ -214,7 +216,11 @@ __device__ __forceinline__ int tile_page(const PageIds& pi, int kt, int m) {
     id = pi.ptab[lp];
     id = id < 0 ? 0 : (id >= pi.num_pages ? pi.num_pages - 1 : id);
   }
-  return __builtin_amdgcn_readfirstlane(id);
+  return id;
+}
+
+__device__ __forceinline__ int tile_page(const PageIds& pi, int kt, int m) {
+  return __builtin_amdgcn_readfirstlane(tile_page_lanes(pi, kt, m));
 }
 
 // Copy one KV tile's K from the pool into an LDS stage, and load its V into
@@ -534,14 +540,16 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
       // the row sum adds the fp32 weights (a sum of their fp16 roundings
       // would be off by up to 2^-11 relative in a row with one dominant
       // key)
-      float ls[4] = {0.f, 0.f, 0.f, 0.f};
+      float ls[4];
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
           const float p0 = fast_exp2(fmaf(sacc[rb][kb2][i], sl2, -mref));
           const float p1 = fast_exp2(fmaf(sacc[rb][kb2][i + 1], sl2, -mref));
-          ls[(i / 2) & 3] += p0 + p1;
+          const int c = (i / 2) & 3;
+          // each chain starts from its first pair (no add of zero)
+          ls[c] = kb2 == 0 && i < 8 ? p0 + p1 : ls[c] + (p0 + p1);
           pk[rb][kb2][i / 2] = pack_f16x2(p0, p1);
         }
       }
@@ -614,7 +622,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
     const int my1 = GRP == 0 ? mid : kt1;
     // The page this wave moves for the next tile is looked up one step
     // ahead (an LDS read whose latency the step's compute hides).
-    auto wave_page = [&](int kt) { return tile_page(pi, min(kt, my1 - 1), wave); };
+    auto wave_page = [&](int kt) { return tile_page_lanes(pi, min(kt, my1 - 1), wave); };
     PageIds direct = pi;
     direct.lds = nullptr;   // the first tile's page comes from the table itself
     VRegs<D> vr;
@@ -625,7 +633,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
     int next_id = wave_page(my0 + 1);
     for (int i = 0;;) {
       int kt = my0 + i;
-      if (kt + 1 < my1) load_tile<D>(ks1, vr, kpool, vpool, next_id, kt + 1, L, Hkv, g, wave, lane);
+      if (kt + 1 < my1)
+        load_tile<D>(ks1, vr, kpool, vpool, __builtin_amdgcn_readfirstlane(next_id), kt + 1, L, Hkv, g, wave, lane);
       next_id = wave_page(kt + 2);
       if (kt < my1) compute_tile(ks0, vs0, kt * kTileKeys);
       __builtin_amdgcn_s_waitcnt(0);
@@ -633,7 +642,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
       __syncthreads();
       if (++i >= nloop) break;
       kt = my0 + i;
-      if (kt + 1 < my1) load_tile<D>(ks0, vr, kpool, vpool, next_id, kt + 1, L, Hkv, g, wave, lane);
+      if (kt + 1 < my1)
+        load_tile<D>(ks0, vr, kpool, vpool, __builtin_amdgcn_readfirstlane(next_id), kt + 1, L, Hkv, g, wave, lane);
       next_id = wave_page(kt + 2);
       if (kt < my1) compute_tile(ks1, vs1, kt * kTileKeys);
       __builtin_amdgcn_s_waitcnt(0);
