@@ -227,10 +227,13 @@ pa_status pa_decode_direct(const pa_desc* desc, const void* q, const void* k_poo
  * request r's n_r query rows (a chunk of a prompt at prior
  * offset q_offsets[r]) attend causally to keys 0 .. q_offsets[r] + i, all of
  * them read from the pages (the chunk's own K/V already appended).  bf16
- * only.  q_starts: int32 [B+1] exclusive prefix sum of n_r, or NULL to derive
- * it on the device.  lse may be NULL.  When the grid is small against the
- * chip, the guard splits long query tiles along their key range and merges
- * the partials by log-sum-exp; that needs `workspace` of at least
+ * only.  The P V product runs in fp16 (weights rounded to fp16, V values
+ * converted from bf16 exactly): V values must lie within fp16's range,
+ * |v| <= 65504; a larger one becomes infinite.  q_starts: int32 [B+1]
+ * exclusive prefix sum of n_r, or NULL to derive it on the device.  lse
+ * may be NULL.  When the grid is small against the chip, the guard splits
+ * long query tiles along their key range and merges the partials by
+ * log-sum-exp; that needs `workspace` of at least
  * pa_plan(...).workspace_bytes bytes (PA_ERR_WORKSPACE if a smaller one is
  * given).  workspace = NULL runs every tile unsplit (always valid, slower on
  * unbalanced batches). */
@@ -252,7 +255,8 @@ pa_status pa_prefill_chunk(const pa_desc* desc, const void* q, const void* k_poo
  * either a 128-row prefill tile or a whole decode (request, KV head), so a
  * step needs one launch instead of a prefill launch, a decode launch and a
  * merge pass, and the MFMA-bound tiles and HBM-bound decode items run on
- * the chip at the same time.  bf16 only; d = 64 or 128; G in {1, 2, 4, 8};
+ * the chip at the same time.  bf16 only (prefill tiles as in
+ * pa_prefill_chunk, V within fp16's range); d = 64 or 128; G in {1, 2, 4, 8};
  * B <= 512 (PA_ERR_UNSUPPORTED otherwise).  No workspace; prefill tiles are
  * never split along their keys, so a batch whose prefill is a few very
  * long chunks is better served by pa_prefill_chunk, which can split.
@@ -360,8 +364,13 @@ pa_status pa_gather_kv(const pa_desc* desc, const void* k_pool, const void* v_po
 /* Debugging aid: copies the metadata to the host (synchronizing `stream`)
  * and checks the device-array contract above (the page table, context
  * lengths and offsets of the "Paged KV Cache" section of the tiny-llm
- * source reading).  q_offsets may be NULL
- * (decode).  Returns PA_OK or PA_ERR_METADATA. */
+ * source reading).  q_offsets may be NULL (decode).  Returns PA_OK or
+ * PA_ERR_METADATA.  With PA_DEBUG_VALIDATE set in the environment (to
+ * anything but "0"; read once per process), pa_decode, pa_decode_noalloc,
+ * pa_split_merge, pa_decode_direct, pa_prefill_chunk, pa_mixed_attention and
+ * pa_append_kv run this check first and return its error instead of
+ * launching; each call then synchronizes its stream, so the switch is for
+ * debugging only. */
 pa_status pa_validate_metadata(const pa_desc* desc, const int32_t* page_table,
                                const int32_t* seq_lens, const int32_t* q_offsets, void* stream);
 

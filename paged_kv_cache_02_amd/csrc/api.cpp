@@ -119,6 +119,19 @@ pa_status check_decode_call(const pa_desc* d, const void* q, const void* k_pool,
 namespace {
 using pa::check_decode_call;
 
+// Debugging switch: with PA_DEBUG_VALIDATE set in the environment (to
+// anything but "0"), every call that reads a page table first checks the
+// device metadata with pa_validate_metadata (a copy to the host and a
+// synchronization of the caller's stream) and returns its error instead of
+// launching.  The variable is read once per process.
+bool debug_validate() {
+  static const bool on = [] {
+    const char* e = getenv("PA_DEBUG_VALIDATE");
+    return e != nullptr && e[0] != '\0' && strcmp(e, "0") != 0;
+  }();
+  return on;
+}
+
 size_t partial_o_bytes(const pa_desc* d, int S) {
   return align_up((size_t)d->num_seqs * d->num_q_heads * (size_t)S * d->head_dim * sizeof(float));
 }
@@ -341,6 +354,8 @@ pa_status pa_decode(const pa_desc* d, const void* q, const void* k_pool, const v
   (void)q_offsets;  // decode rows sit at position seq_len - 1 by contract
   pa_status st = check_decode_call(d, q, k_pool, v_pool, page_table, seq_lens, scale, out, lse);
   if (st != PA_OK || d->num_seqs == 0) return st;
+  if (debug_validate() && (st = pa_validate_metadata(d, page_table, seq_lens, nullptr, stream)) != PA_OK)
+    return st;
   pa_plan_info plan;
   st = pa_plan(d, 0, &plan);
   if (st != PA_OK) return st;
@@ -388,6 +403,8 @@ pa_status pa_decode_direct(const pa_desc* d, const void* q, const void* k_pool, 
                            float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   pa_status st = check_decode_call(d, q, k_pool, v_pool, page_table, seq_lens, scale, out, lse);
   if (st != PA_OK || d->num_seqs == 0) return st;
+  if (debug_validate() && (st = pa_validate_metadata(d, page_table, seq_lens, nullptr, stream)) != PA_OK)
+    return st;
   const int Gd = d->num_q_heads / d->num_kv_heads;
   if (!(Gd == 1 || Gd == 2 || Gd == 4 || Gd == 8)) return PA_ERR_UNSUPPORTED;
   if (workspace == nullptr || workspace_bytes < pa_direct_workspace_bytes(d) || !aligned16(workspace))
@@ -425,6 +442,8 @@ pa_status pa_split_merge(const pa_desc* d, const void* q, const void* k_pool, co
   if (st != PA_OK) return st;
   if (num_splits < 1 || num_splits > kMaxSplitsApi) return PA_ERR_ARG;
   if (d->num_seqs == 0) return PA_OK;
+  if (debug_validate() && (st = pa_validate_metadata(d, page_table, seq_lens, nullptr, stream)) != PA_OK)
+    return st;
   const size_t need = pa_workspace_bytes(d, num_splits);
   if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return PA_ERR_WORKSPACE;
   pa::DecodeArgs a = decode_args(d, q, k_pool, v_pool, page_table, seq_lens, scale);
@@ -449,6 +468,8 @@ pa_status pa_prefill_chunk(const pa_desc* d, const void* q, const void* k_pool,
   if (out == q) return PA_ERR_ARG;
   if (!(scale > 0.f) || !isfinite(scale)) return PA_ERR_ARG;
   if (d->max_q_len < 1) return PA_ERR_ARG;
+  if (debug_validate() && (st = pa_validate_metadata(d, page_table, seq_lens, q_offsets, stream)) != PA_OK)
+    return st;
   PrefillPlan pp = prefill_plan(d, device_cu_count());
   if (workspace == nullptr) {
     // no scratch: run every query tile over its whole key range
@@ -507,6 +528,8 @@ pa_status pa_mixed_attention(const pa_desc* d, const void* q, const void* k_pool
   if (out == q) return PA_ERR_ARG;
   if (!(scale > 0.f) || !isfinite(scale)) return PA_ERR_ARG;
   if (d->max_q_len < 1) return PA_ERR_ARG;
+  if (debug_validate() && (st = pa_validate_metadata(d, page_table, seq_lens, q_offsets, stream)) != PA_OK)
+    return st;
   pa::PrefillArgs a;
   memset(&a, 0, sizeof(a));
   a.q = q;
@@ -548,6 +571,8 @@ pa_status pa_append_kv(const pa_desc* d, const void* k_new, const void* v_new,
       (q_starts && !aligned4(q_starts)))
     return PA_ERR_ARG;
   if (d->max_q_len < 1) return PA_ERR_ARG;
+  if (debug_validate() && (st = pa_validate_metadata(d, page_table, seq_lens, q_offsets, stream)) != PA_OK)
+    return st;
   pa::AppendArgs a;
   memset(&a, 0, sizeof(a));
   a.k_new = k_new;

@@ -146,6 +146,8 @@ static void check_pool_invariants(pa_page_pool* p, int NP) {
   CHECK(pa_pool_num_free(p) == NP - held);
 }
 
+static int count_bad_launches(bool expect_validation);
+
 static int asan_mode() {
   std::mt19937 rng(1234);
   // ---- the dispatch guard on random descriptors: never a crash, plans
@@ -227,6 +229,9 @@ static int asan_mode() {
     sl[2] = 0;             // empty request
     CHECK(pa_validate_metadata(&x, pt.data(), sl.data(), qo.data(), nullptr) == PA_ERR_METADATA);
   }
+
+  // ---- without PA_DEBUG_VALIDATE, bad device metadata is not looked at
+  CHECK(count_bad_launches(false) > 0);
 
   // ---- the pool, single thread: random operations against invariants
   {
@@ -339,7 +344,73 @@ static int tsan_mode() {
   return 0;
 }
 
+// ---------------------------------------------------------------------------
+// debug mode (run with PA_DEBUG_VALIDATE=1 in the environment): every call
+// that reads a page table checks the metadata first, launches nothing and
+// returns PA_ERR_METADATA when it is bad, and launches as usual when it is
+// good; without the variable (asan mode) the same bad metadata launches
+// ---------------------------------------------------------------------------
+static int count_bad_launches(bool expect_validation) {
+  const int B = 3, MP = 8, NP = 32;
+  std::vector<int32_t> pt(B * MP, -1), sl = {20, 33, 5}, qo = {18, 30, 0};
+  int next = 0;
+  for (int r = 0; r < B; ++r)
+    for (int p = 0; p < (sl[r] + 15) / 16; ++p) pt[r * MP + p] = next++;
+  alignas(16) static char buf[1 << 16];
+  char* q = buf;
+  char* kp = buf + 8192;
+  char* vp = buf + 16384;
+  char* out = buf + 24576;
+  float* lse = reinterpret_cast<float*>(buf + 32768);
+  const pa_status bad = expect_validation ? PA_ERR_METADATA : PA_OK;
+  // chunks: 2 + 3 + 5 query rows
+  pa_desc x = make(B, 8, 2, 64, NP, MP, 10, 100, 5, PA_BF16);
+  auto prefill = [&] {
+    return pa_prefill_chunk(&x, q, kp, vp, pt.data(), sl.data(), qo.data(), nullptr, 0.1f, out, lse,
+                            nullptr, 0, nullptr);
+  };
+  auto mixed = [&] {
+    return pa_mixed_attention(&x, q, kp, vp, pt.data(), sl.data(), qo.data(), nullptr, 0.1f, out, lse,
+                              nullptr);
+  };
+  auto append = [&] {
+    return pa_append_kv(&x, q, out, pt.data(), sl.data(), qo.data(), nullptr, kp, vp, nullptr);
+  };
+  int n = g_launches.load();
+  CHECK(prefill() == PA_OK && mixed() == PA_OK && append() == PA_OK);
+  CHECK(g_launches.load() == n + 3);
+  pt[1 * MP + 2] = NP;   // a page id past the pool
+  n = g_launches.load();
+  CHECK(prefill() == bad && mixed() == bad && append() == bad);
+  const int prefill_launches = g_launches.load() - n;
+  pt[1 * MP + 2] = 4;
+  // decode rows: one per request at position seq_len - 1
+  pa_desc y = make(B, 8, 2, 64, NP, MP, B, 100, 1, PA_BF16);
+  pa_plan_info plan;
+  CHECK(pa_plan(&y, 0, &plan) == PA_OK);
+  std::vector<char> ws(plan.workspace_bytes + 256);
+  char* w = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(ws.data()) + 255) & ~uintptr_t(255));
+  auto decode = [&] {
+    return pa_decode(&y, q, kp, vp, pt.data(), sl.data(), nullptr, 0.1f, out, lse, w, plan.workspace_bytes,
+                     nullptr);
+  };
+  n = g_launches.load();
+  CHECK(decode() == PA_OK);
+  CHECK(g_launches.load() > n);
+  sl[2] = 0;   // an empty request
+  n = g_launches.load();
+  CHECK(decode() == bad);
+  return prefill_launches + (g_launches.load() - n);
+}
+
+static int debug_mode() {
+  CHECK(count_bad_launches(true) == 0);
+  std::printf("debug mode ok\n");
+  return 0;
+}
+
 int main(int argc, char** argv) {
   if (argc > 1 && std::strcmp(argv[1], "tsan") == 0) return tsan_mode();
+  if (argc > 1 && std::strcmp(argv[1], "debug") == 0) return debug_mode();
   return asan_mode();
 }

@@ -3,7 +3,9 @@ carving, metadata validation, page allocator) built with g++ under
 AddressSanitizer + UndefinedBehaviorSanitizer and, for the allocator shared
 by eight threads, under ThreadSanitizer; tests/host/harness.cpp holds the
 checks and the stubs that stand in for the HIP runtime and the kernels.
-CPU only."""
+The PA_DEBUG_VALIDATE switch (metadata checked before every launch that
+reads a page table) is tested in a process of its own, since the library
+reads the variable once.  CPU only."""
 import os
 import shutil
 import subprocess
@@ -26,7 +28,8 @@ def build_and_run(tmp_path, flags, mode, env_extra):
     cmd = ["g++", *COMMON, *flags, *SRCS, "-o", exe]
     res = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
     assert res.returncode == 0, res.stderr[-4000:]
-    env = dict(os.environ, **env_extra)
+    env = {k: v for k, v in os.environ.items() if k != "PA_DEBUG_VALIDATE"}
+    env.update(env_extra)
     run = subprocess.run([exe, mode], capture_output=True, text=True, timeout=300, env=env)
     print(run.stdout, run.stderr[-3000:])
     assert run.returncode == 0, run.stderr[-4000:]
@@ -45,3 +48,9 @@ def test_host_code_under_address_and_undefined_sanitizers(tmp_path):
 def test_page_pool_under_thread_sanitizer(tmp_path):
     out = build_and_run(tmp_path, ["-fsanitize=thread"], "tsan", {"TSAN_OPTIONS": "halt_on_error=1"})
     assert "tsan mode ok" in out
+
+
+def test_debug_validation_switch(tmp_path):
+    out = build_and_run(tmp_path, ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined"],
+                        "debug", {"PA_DEBUG_VALIDATE": "1", "ASAN_OPTIONS": "detect_leaks=1:abort_on_error=0"})
+    assert "debug mode ok" in out
