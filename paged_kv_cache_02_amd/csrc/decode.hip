@@ -109,6 +109,29 @@ __device__ void page_prefix(int* pre, const int32_t* __restrict__ seq_lens, int 
   __syncthreads();
 }
 
+// Small batches (B <= kWaveSeqs): every wave computes the prefix on its own,
+// one request per lane, into its own row of `pre` (kWaveSeqs + 1 ints per
+// wave) and reads it back itself, so no workgroup barrier and no exchange
+// between waves is needed.  The scan is the usual wave-64 one: inclusive
+// within rows of 16 lanes by DPP row shifts, then carried across rows by the
+// row-15 and row-31 broadcasts.  Returns the wave's row.
+constexpr int kWaveSeqs = 64;
+__device__ int* page_prefix_wave(int* pre, const int32_t* __restrict__ seq_lens, int B, int max_pages,
+                                 int wave, int lane) {
+  int* row = pre + wave * (kWaveSeqs + 1);
+  int x = lane < B ? pages_of(seq_lens[lane], max_pages) : 0;
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31 into rows 2, 3
+  if (lane == 0) row[0] = 0;
+  if (lane < B) row[lane + 1] = x;
+  __builtin_amdgcn_wave_barrier();
+  return row;
+}
+
 // The metadata and the partial outputs come as separate restrict parameters:
 // with them the compiler can prove that the kernel's own stores never touch
 // the page table, and reads page ids with scalar loads (a vector load there
@@ -123,7 +146,7 @@ decode_balanced_kernel(DecodeArgs a, const int32_t* __restrict__ page_table,
   using P = Pipe<T, D, G, G * S::kChunksPerLane * 4>;
   constexpr int kDepth = P::kDepth;
   constexpr int kBufs = P::kBufs;
-  __shared__ int pre[kMaxBalancedSeqs + 1];
+  __shared__ int pre_lds[kMaxBalancedSeqs + 1];
 
   const int32_t num_pages = a.num_pages;
   const int lane = threadIdx.x & 63;
@@ -138,7 +161,12 @@ decode_balanced_kernel(DecodeArgs a, const int32_t* __restrict__ page_table,
   const int g = blockIdx.x % Hkv;
   const int v = (blockIdx.x / Hkv) * kWaves + wave;
 
-  page_prefix(pre, seq_lens, B, maxp);
+  // pre[r] = pages of requests 0 .. r-1, for r in [0, B]
+  int* pre = pre_lds;
+  if (B <= kWaveSeqs)
+    pre = page_prefix_wave(pre_lds, seq_lens, B, maxp, wave, lane);
+  else
+    page_prefix(pre_lds, seq_lens, B, maxp);
   const int N = uniform(pre[B]);
   const int per = N > 0 ? (N + V - 1) / V : 1;  // pages per wave range
 
@@ -342,7 +370,7 @@ decode_mfma_kernel(DecodeArgs a, const int32_t* __restrict__ page_table,
   // or three, or 1-2% faster; d = 64 runs two workgroups per CU with three
   constexpr int kDepth = D >= 128 ? 1 : 3;
   constexpr int kBufs = kDepth + 1;
-  __shared__ int pre[kMaxBalancedSeqs + 1];
+  __shared__ int pre_lds[kMaxBalancedSeqs + 1];
   __shared__ __align__(16) unsigned char vslots[kWaves][kPageSize * M::kRowBytes];
 
   const int32_t num_pages = a.num_pages;
@@ -357,7 +385,12 @@ decode_mfma_kernel(DecodeArgs a, const int32_t* __restrict__ page_table,
   const int v = (blockIdx.x / Hkv) * kWaves + wave;
   unsigned char* vslot = vslots[wave];
 
-  page_prefix(pre, seq_lens, B, maxp);
+  // pre[r] = pages of requests 0 .. r-1, for r in [0, B]
+  int* pre = pre_lds;
+  if (B <= kWaveSeqs)
+    pre = page_prefix_wave(pre_lds, seq_lens, B, maxp, wave, lane);
+  else
+    page_prefix(pre_lds, seq_lens, B, maxp);
   const int N = uniform(pre[B]);
   const int per = N > 0 ? (N + V - 1) / V : 1;  // pages per wave range
 
