@@ -117,9 +117,10 @@ __device__ void page_prefix(int* pre, const int32_t* __restrict__ seq_lens, int 
 // row-15 and row-31 broadcasts.  Returns the wave's row.
 constexpr int kWaveSeqs = 64;
 __device__ int* page_prefix_wave(int* pre, const int32_t* __restrict__ seq_lens, int B, int max_pages,
-                                 int wave, int lane) {
+                                 int wave, int lane, int& excl) {
   int* row = pre + wave * (kWaveSeqs + 1);
-  int x = lane < B ? pages_of(seq_lens[lane], max_pages) : 0;
+  const int np = lane < B ? pages_of(seq_lens[lane], max_pages) : 0;
+  int x = np;
   x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
   x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
   x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
@@ -129,7 +130,23 @@ __device__ int* page_prefix_wave(int* pre, const int32_t* __restrict__ seq_lens,
   if (lane == 0) row[0] = 0;
   if (lane < B) row[lane + 1] = x;
   __builtin_amdgcn_wave_barrier();
+  excl = x - np;   // pre[lane]
   return row;
+}
+
+// The request holding page f0: the largest r < B with pre[r] <= f0 (pre is
+// non-decreasing and pre[0] = 0).  Small batches count it from the lanes'
+// exclusive prefixes with one ballot; others search the LDS prefix.
+__device__ __forceinline__ int request_of_page(const int* pre, int B, int f0, bool small, int excl,
+                                               int lane) {
+  if (small) return __popcll(__ballot(lane >= 1 && lane < B && excl <= f0));
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (uniform(pre[mid]) <= f0) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
 }
 
 // The metadata and the partial outputs come as separate restrict parameters:
@@ -163,8 +180,10 @@ decode_balanced_kernel(DecodeArgs a, const int32_t* __restrict__ page_table,
 
   // pre[r] = pages of requests 0 .. r-1, for r in [0, B]
   int* pre = pre_lds;
-  if (B <= kWaveSeqs)
-    pre = page_prefix_wave(pre_lds, seq_lens, B, maxp, wave, lane);
+  int excl = 0;
+  const bool small = B <= kWaveSeqs;
+  if (small)
+    pre = page_prefix_wave(pre_lds, seq_lens, B, maxp, wave, lane, excl);
   else
     page_prefix(pre_lds, seq_lens, B, maxp);
   const int N = uniform(pre[B]);
@@ -196,13 +215,7 @@ decode_balanced_kernel(DecodeArgs a, const int32_t* __restrict__ page_table,
     return L < maxp * kPageSize ? L : maxp * kPageSize;
   };
 
-  // request holding page f0: the largest r with pre[r] <= f0
-  int lo = 0, hi = B - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (uniform(pre[mid]) <= f0) lo = mid;
-    else hi = mid - 1;
-  }
+  const int lo = uniform(request_of_page(pre, B, f0, small, excl, lane));
 
   const T* __restrict__ qp = reinterpret_cast<const T*>(a.q);
   const T* __restrict__ kpool = reinterpret_cast<const T*>(a.k_pool);
@@ -387,8 +400,10 @@ decode_mfma_kernel(DecodeArgs a, const int32_t* __restrict__ page_table,
 
   // pre[r] = pages of requests 0 .. r-1, for r in [0, B]
   int* pre = pre_lds;
-  if (B <= kWaveSeqs)
-    pre = page_prefix_wave(pre_lds, seq_lens, B, maxp, wave, lane);
+  int excl = 0;
+  const bool small = B <= kWaveSeqs;
+  if (small)
+    pre = page_prefix_wave(pre_lds, seq_lens, B, maxp, wave, lane, excl);
   else
     page_prefix(pre_lds, seq_lens, B, maxp);
   const int N = uniform(pre[B]);
@@ -417,12 +432,8 @@ decode_mfma_kernel(DecodeArgs a, const int32_t* __restrict__ page_table,
     const int L = seq_lens[r];
     return L < maxp * kPageSize ? L : maxp * kPageSize;
   };
-  int lo = 0, hi = B - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (uniform(pre[mid]) <= f0) lo = mid;
-    else hi = mid - 1;
-  }
+  // request holding page f0
+  const int lo = uniform(request_of_page(pre, B, f0, small, excl, lane));
 
   const __bf16* __restrict__ qp = reinterpret_cast<const __bf16*>(a.q);
   const __bf16* __restrict__ kpool = reinterpret_cast<const __bf16*>(a.k_pool);
