@@ -673,6 +673,14 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
   // the running max and sum follow the float4s in the same buffer
   constexpr int kMlOff = kHalf * 4 * 1024;
   static_assert(kMlOff + 2 * 64 * 4 <= GE::kTileBytes, "exchange fits a stage buffer");
+  // the final rows go out through a wave-private region after the exchange
+  // data: 32 rows x kHalf * 64 bytes of bf16, 16-byte chunks XOR-swizzled
+  // by row
+  constexpr int kRowB = kHalf * 64;          // bytes of a row's half
+  constexpr int kChunks = kRowB / 16;        // 16-byte chunks per row half
+  constexpr int kRowsPerStore = 64 / kChunks;
+  constexpr int kTransOff = kMlOff + 2 * 64 * 4;
+  static_assert(kTransOff + 32 * kRowB <= GE::kTileBytes, "transpose region fits a stage buffer");
   auto finish = [&](auto gtag) __attribute__((always_inline)) {
     constexpr int GRP = decltype(gtag)::value;
     constexpr int kKeep = GRP == 0 ? 0 : kHalf;   // first dim block this group keeps
@@ -728,26 +736,55 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
       const float l_tot = pair_sum(l_run[rb]);
-      if (!row_valid[rb]) continue;
       const bool empty = !(l_tot > 0.f);
       const float inv = empty ? 0.f : 1.f / l_tot;
       const float lse = empty ? -INFINITY : (m_run[rb] + __log2f(l_tot)) * kLn2;
       if (!partial) {
-        __bf16* orow = reinterpret_cast<__bf16*>(a.out) +
-                       ((size_t)(q_start + tok[rb]) * Hq + (size_t)g * group + hh[rb]) * D;
+        // Each lane writes its pieces of its row into the wave's region,
+        // then reads 16 contiguous bytes of one row: a store instruction
+        // then writes whole row halves (kRowsPerStore rows of kRowB bytes)
+        // instead of 16 bytes in each of 32 rows.  Only this wave touches
+        // the region, and its LDS operations complete in order.
+        unsigned char* tp = mine + kTransOff;
 #pragma unroll
         for (int j = 0; j < kHalf; ++j)
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             const int db = kKeep + j;
+            const int c = 4 * j + v;   // 16-byte chunk of the row half (8 dims)
             uint2 w;
             w.x = pack_bf16x2(oacc[rb][db][4 * v + 0] * inv, oacc[rb][db][4 * v + 1] * inv);
             w.y = pack_bf16x2(oacc[rb][db][4 * v + 2] * inv, oacc[rb][db][4 * v + 3] * inv);
-            *reinterpret_cast<uint2*>(orow + db * 32 + 8 * v + 4 * half) = w;
+            *reinterpret_cast<uint2*>(tp + lrow * kRowB + ((c ^ (lrow & (kChunks - 1))) * 16) + 8 * half) = w;
           }
-        if (GRP == 0 && a.lse != nullptr && half == 0)
+        // output row of this lane's row (lanes 0-31 hold rows 0-31), or -1
+        const int out_row =
+            row_valid[rb] ? (q_start + tok[rb]) * Hq + g * group + hh[rb] : -1;
+        __builtin_amdgcn_wave_barrier();
+        constexpr int kStores = 32 / kRowsPerStore;
+        const int cc = lane % kChunks;
+        uint4 x[kStores];
+        int orr[kStores];
+#pragma unroll
+        for (int i = 0; i < kStores; ++i) {   // all reads first, then the stores
+          const int rr = lane / kChunks + i * kRowsPerStore;
+          x[i] = *reinterpret_cast<const uint4*>(tp + rr * kRowB + ((cc ^ (rr & (kChunks - 1))) * 16));
+          orr[i] = __shfl(out_row, rr);
+        }
+        // keep the reads ahead of the conditional stores (left alone, the
+        // compiler sinks each read into its store's branch, one LDS round
+        // trip after another)
+#pragma unroll
+        for (int i = 0; i < kStores; ++i) asm volatile("" : "+v"(x[i].x), "+v"(x[i].y), "+v"(x[i].z), "+v"(x[i].w));
+#pragma unroll
+        for (int i = 0; i < kStores; ++i)
+          if (orr[i] >= 0)
+            *reinterpret_cast<uint4*>(reinterpret_cast<__bf16*>(a.out) + (size_t)orr[i] * D + kKeep * 32 + cc * 8) =
+                x[i];
+        if (GRP == 0 && a.lse != nullptr && half == 0 && row_valid[rb])
           a.lse[(size_t)(q_start + tok[rb]) * Hq + (size_t)g * group + hh[rb]] = lse;
       } else {
+        if (!row_valid[rb]) continue;
         const int prow = wave * kRowsPerWave + rb * 32 + lrow;   // row within the tile
         const size_t pidx = (unit * S + split) * kTileRows + prow;
         float* po = a.part_o + pidx * D;
