@@ -381,14 +381,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
   const int pos_hi = o + wrow1 / group;
 
   const __bf16* __restrict__ qp = reinterpret_cast<const __bf16*>(a.q);
+  // this lane's query operand registers, filled from LDS in run()
   uint4 qv[kRB][GE::kKSteps];
-#pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) {
-    const __bf16* qrow = qp + ((size_t)(q_start + tok[rb]) * Hq + (size_t)g * group + hh[rb]) * D;
-#pragma unroll
-    for (int s = 0; s < GE::kKSteps; ++s)
-      qv[rb][s] = *reinterpret_cast<const uint4*>(qrow + 16 * s + 8 * half);
-  }
 
   const __bf16* __restrict__ kpool = reinterpret_cast<const __bf16*>(a.k_pool);
   const __bf16* __restrict__ vpool = reinterpret_cast<const __bf16*>(a.v_pool);
@@ -625,11 +619,43 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
     auto wave_page = [&](int kt) { return tile_page_lanes(pi, min(kt, my1 - 1), wave); };
     PageIds direct = pi;
     direct.lds = nullptr;   // the first tile's page comes from the table itself
+    // The wave's 32 query rows come in by DMA, whole rows per instruction,
+    // into the slices of the stage-1 K and V buffers that this wave's own
+    // copies overwrite first (rows 0-15 in the K slice, 16-31 in the V
+    // slice), laid out like K rows (16-byte chunks XOR-swizzled by row).
+    // They are read into registers after the first barrier and waited for
+    // before this wave's first copy into stage 1, so no other wave is
+    // involved.
+    constexpr int kSlice = (GE::kDmaPerTile / kWavesPerGroup) * 1024;   // a wave's part of a stage
+    static_assert(16 * GE::kRowBytes == kSlice, "16 query rows fill a wave's slice");
+    unsigned char* qk = ks1 + wave * kSlice;
+    unsigned char* qvs = vs1 + wave * kSlice;
+#pragma unroll
+    for (int i = 0; i < 32 / GE::kKeysPerDma; ++i) {
+      const int row = i * GE::kKeysPerDma + lane / GE::kRowChunks;   // of the wave's 32
+      const int rho0 = tg.row_base + wave * kRowsPerWave + row;
+      const int rho = rho0 < tg.rows_total ? rho0 : tg.rows_total - 1;
+      const int chunk = (lane % GE::kRowChunks) ^ swz<D>(row);
+      const __bf16* src = qp + ((size_t)(q_start + rho / group) * Hq + (size_t)g * group + rho % group) * D +
+                          chunk * 8;
+      unsigned char* dst = (row < 16 ? qk : qvs) + (i % (16 / GE::kKeysPerDma)) * 1024;
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
+    }
     VRegs<D> vr;
     if (my0 < my1) load_tile<D>(ks0, vr, kpool, vpool, tile_page(direct, my0, wave), my0, L, Hkv, g, wave, lane);
     __builtin_amdgcn_s_waitcnt(0);
     if (my0 < my1) store_v<D>(vs0, vr, wave, lane);
-    __syncthreads();   // stage 0 and the page ids in LDS
+    __syncthreads();   // stage 0, the query rows and the page ids in LDS
+    {
+      const int sw = swz<D>(lrow);
+      const uint32_t qbase = (uint32_t)((lrow & 15) * GE::kRowBytes) + ((uint32_t)(half ^ (sw & 1)) << 4) +
+                             ((uint32_t)(sw >> 1) << 5);
+      const unsigned char* qsrc = lrow < 16 ? qk : qvs;
+#pragma unroll
+      for (int s = 0; s < GE::kKSteps; ++s)
+        qv[0][s] = *reinterpret_cast<const uint4*>(qsrc + (qbase ^ (uint32_t)(s << 5)));
+      __builtin_amdgcn_s_waitcnt(0);   // read before this wave's first copy into stage 1
+    }
     int next_id = wave_page(my0 + 1);
     for (int i = 0;;) {
       int kt = my0 + i;
