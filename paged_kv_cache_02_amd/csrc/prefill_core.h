@@ -394,6 +394,50 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
   pi.npages = npages;
   pi.num_pages = a.num_pages;
   pi.lds = nullptr;
+  // The wave's 32 query rows come in by DMA, whole rows per instruction,
+  // into the slices of its group's stage-1 K and V buffers that this wave's
+  // own copies overwrite first (rows 0-15 in the K slice, 16-31 in the V
+  // slice), laid out like K rows (16-byte chunks XOR-swizzled by row).  They
+  // are read into registers after the first barrier and waited for before
+  // this wave's first copy into stage 1, so no other wave is involved.  The
+  // group's first tile's page id is read straight from the table here too,
+  // so both reads are in flight with the page-id copy below (the raw entry
+  // is clamped only where it is used).
+  constexpr int kSlice = (GE::kDmaPerTile / kWavesPerGroup) * 1024;   // a wave's part of a stage
+  static_assert(16 * GE::kRowBytes == kSlice, "16 query rows fill a wave's slice");
+  unsigned char* const qk = (grp == 0 ? k_a1 : k_b1) + wave * kSlice;
+  unsigned char* const qvs = (grp == 0 ? v_a1 : v_b1) + wave * kSlice;
+  // packed row -> (token, head): rho / group by a multiply with the rounded-up
+  // reciprocal, exact while rho * group < 2^32 (else a plain division)
+  auto load_q_rows = [&](auto div) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 32 / GE::kKeysPerDma; ++i) {
+      const int row = i * GE::kKeysPerDma + lane / GE::kRowChunks;   // of the wave's 32
+      const int rho0 = tg.row_base + wave * kRowsPerWave + row;
+      const int rho = rho0 < tg.rows_total ? rho0 : tg.rows_total - 1;
+      const int tk = div(rho);
+      const int hd = rho - tk * group;
+      const int chunk = (lane % GE::kRowChunks) ^ swz<D>(row);
+      const __bf16* src = qp + ((size_t)(q_start + tk) * Hq + (size_t)g * group + hd) * D + chunk * 8;
+      unsigned char* dst = (row < 16 ? qk : qvs) + (i % (16 / GE::kKeysPerDma)) * 1024;
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
+    }
+  };
+  if (group == 1) {
+    load_q_rows([&](int rho) { return rho; });
+  } else if ((unsigned long long)tg.rows_total * (unsigned)group < 0x100000000ull) {
+    // ceil(2^32 / group) fits 32 bits for group >= 2
+    const uint32_t gmul = (uint32_t)((0x100000000ull + (uint32_t)group - 1) / (uint32_t)group);
+    load_q_rows([&](int rho) { return (int)__umulhi((uint32_t)rho, gmul); });
+  } else {
+    load_q_rows([&](int rho) { return rho / group; });
+  }
+  const int mid = kt0 + (kt1 - kt0 + 1) / 2;
+  const int first_kt = grp == 0 ? kt0 : mid;
+  const int first_lp = first_kt * kPagesPerTile + wave;
+  const bool first_valid = first_kt < (grp == 0 ? mid : kt1) && first_lp < npages;
+  const int first_raw = first_valid ? ptab[first_lp] : -1;
+
   const int p0 = kt0 * kPagesPerTile;
   const int p1 = min(kt1 * kPagesPerTile, npages);
   if (p1 - p0 <= kLdsPages) {
@@ -604,7 +648,6 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
   // per step (shared by both groups, which run the same number of steps)
   // hands stages over.  Unrolled by two so each step names its stages.
   const int L = tg.L;
-  const int mid = kt0 + (kt1 - kt0 + 1) / 2;
   const int nloop = mid - kt0;
   auto run = [&](auto gtag) __attribute__((always_inline)) {
     constexpr int GRP = decltype(gtag)::value;
@@ -617,32 +660,15 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
     // The page this wave moves for the next tile is looked up one step
     // ahead (an LDS read whose latency the step's compute hides).
     auto wave_page = [&](int kt) { return tile_page_lanes(pi, min(kt, my1 - 1), wave); };
-    PageIds direct = pi;
-    direct.lds = nullptr;   // the first tile's page comes from the table itself
-    // The wave's 32 query rows come in by DMA, whole rows per instruction,
-    // into the slices of the stage-1 K and V buffers that this wave's own
-    // copies overwrite first (rows 0-15 in the K slice, 16-31 in the V
-    // slice), laid out like K rows (16-byte chunks XOR-swizzled by row).
-    // They are read into registers after the first barrier and waited for
-    // before this wave's first copy into stage 1, so no other wave is
-    // involved.
-    constexpr int kSlice = (GE::kDmaPerTile / kWavesPerGroup) * 1024;   // a wave's part of a stage
-    static_assert(16 * GE::kRowBytes == kSlice, "16 query rows fill a wave's slice");
-    unsigned char* qk = ks1 + wave * kSlice;
-    unsigned char* qvs = vs1 + wave * kSlice;
-#pragma unroll
-    for (int i = 0; i < 32 / GE::kKeysPerDma; ++i) {
-      const int row = i * GE::kKeysPerDma + lane / GE::kRowChunks;   // of the wave's 32
-      const int rho0 = tg.row_base + wave * kRowsPerWave + row;
-      const int rho = rho0 < tg.rows_total ? rho0 : tg.rows_total - 1;
-      const int chunk = (lane % GE::kRowChunks) ^ swz<D>(row);
-      const __bf16* src = qp + ((size_t)(q_start + rho / group) * Hq + (size_t)g * group + rho % group) * D +
-                          chunk * 8;
-      unsigned char* dst = (row < 16 ? qk : qvs) + (i % (16 / GE::kKeysPerDma)) * 1024;
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
-    }
     VRegs<D> vr;
-    if (my0 < my1) load_tile<D>(ks0, vr, kpool, vpool, tile_page(direct, my0, wave), my0, L, Hkv, g, wave, lane);
+    if (my0 < my1) {
+      int id = -1;
+      if (first_valid) {
+        id = __builtin_amdgcn_readfirstlane(first_raw);
+        id = id < 0 ? 0 : (id >= a.num_pages ? a.num_pages - 1 : id);
+      }
+      load_tile<D>(ks0, vr, kpool, vpool, id, my0, L, Hkv, g, wave, lane);
+    }
     __builtin_amdgcn_s_waitcnt(0);
     if (my0 < my1) store_v<D>(vs0, vr, wave, lane);
     __syncthreads();   // stage 0, the query rows and the page ids in LDS
