@@ -27,6 +27,7 @@ import ctypes
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -262,11 +263,24 @@ def config_sweep(iters: int, warmup: int):
         torch.cuda.empty_cache()
 
 
+_TOKEN = re.compile(r'"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'|//[^\n]*|/\*.*?\*/', re.S)
+
+
+def code_text(src: str) -> str:
+    """C++ source with its comments removed and whitespace runs collapsed,
+    so an edit to comments or layout alone leaves the hash unchanged."""
+    def keep(m):
+        t = m.group(0)
+        return " " if t.startswith("/") else t
+    return " ".join(_TOKEN.sub(keep, src).split())
+
+
 def source_hash(*names) -> str:
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "paged_kv_cache_02_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "paged_kv_cache_02_amd", "csrc", n), encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode())
+        h.update(b"\0")
     return h.hexdigest()[:16]
 
 

@@ -18,9 +18,9 @@
 // and write partial results, combined by a merge pass.
 //
 // Keys stream in tiles of 64 (4 pages); per wave group and KV tile:
-//   * K pages are copied straight from HBM into LDS with global_load_lds (no
-//     staging registers), double-buffered one tile ahead, K's 16-byte chunks
-//     XOR-swizzled by key; V pages are loaded into registers at the same
+//   * K pages are copied straight from HBM into LDS by buffer loads with
+//     the LDS flag (no staging registers), double-buffered one tile ahead,
+//     K's 16-byte chunks XOR-swizzled by key; V pages are loaded into registers at the same
 //     time and, once they have landed, converted from bf16 to fp16 and
 //     written to the other LDS stage as [dim block][key] within each 1 KB
 //     piece.  The operand reads below are bank-conflict free, and every
