@@ -590,6 +590,7 @@ pa_status pa_append_kv(const pa_desc* d, const void* k_new, const void* v_new,
   a.head_bytes = d->head_dim * elem_bytes(d->dtype);
   const int rpw = pa::append_rows_per_wg();
   a.tiles_per_seq = (d->max_q_len + rpw - 1) / rpw;
+  a.total_rows = d->total_q;
   return pa::launch_append(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK
                                                                                     : PA_ERR_HIP;
 }

@@ -8,10 +8,16 @@
 // pages come from a shared pool and a page table maps each request's logical
 // sequence onto them).  The copy is bit-exact.
 //
-// One workgroup per (request, group of kRowsPerWg of its new rows); its
-// threads stride over the 16-byte chunks of those rows, K and V alike.  Rows
-// are packed by request then token, as the attention entry points pack their
-// queries.  A page id outside [0, num_pages) is a contract violation: the
+// Rows are packed by request then token, as the attention entry points pack
+// their queries.  When the caller passes the requests' first rows
+// (q_starts) and the batch has at most kThreads requests, one workgroup
+// takes each kRowsPerWg consecutive packed rows: its threads read every
+// request's first row, length and offset at once, mark in LDS which request
+// owns each of its rows, then stride over the 16-byte chunks of the rows, K
+// and V alike.  The grid then has one workgroup per kRowsPerWg rows of the
+// step, however the rows split over requests.  Otherwise one workgroup per
+// (request, group of kRowsPerWg of its new rows) does the same for one
+// request.  A page id outside [0, num_pages) is a contract violation: the
 // row is skipped, so a bad table can never make the kernel write outside the
 // pool.
 #include "pa_internal.h"
@@ -85,6 +91,62 @@ __global__ void __launch_bounds__(kThreads) append_kernel(AppendArgs a) {
   }
 }
 
+// Packed rows [x0, x0 + kRowsPerWg) of the step: every request r (one per
+// thread) whose rows [q_starts[r], q_starts[r] + n_r) meet the range marks
+// the rows it owns with (r + 1, position); the largest r wins where
+// inconsistent metadata makes two requests claim a row.  Rows past total_q
+// are never touched, so no metadata can make this kernel read past k_new.
+__global__ void __launch_bounds__(kThreads) append_flat_kernel(AppendArgs a) {
+  __shared__ unsigned long long s_owner[kRowsPerWg];
+  const int tid = threadIdx.x;
+  const long long x0 = (long long)blockIdx.x * kRowsPerWg;
+  const int rows = a.total_rows - x0 < kRowsPerWg ? (int)(a.total_rows - x0) : kRowsPerWg;
+  if (tid < kRowsPerWg) s_owner[tid] = 0ull;
+  __syncthreads();
+  if (tid < a.num_seqs) {
+    const long long st = a.q_starts[tid];
+    const int L = a.seq_lens[tid];
+    const int o = a.q_offsets[tid];
+    const int n = L - o;
+    if (o >= 0 && n > 0) {
+      const long long lo = st > x0 ? st : x0;
+      const long long hi = st + n < x0 + rows ? st + n : x0 + rows;
+      for (long long x = lo; x < hi; ++x)
+        atomicMax(&s_owner[x - x0], ((unsigned long long)(tid + 1) << 32) | (unsigned)(o + (int)(x - st)));
+    }
+  }
+  __syncthreads();
+
+  const int row_bytes = a.num_kv_heads * a.head_bytes;
+  const int row_chunks = row_bytes / 16;
+  const int head_chunks = a.head_bytes / 16;
+  const unsigned char* __restrict__ kn = reinterpret_cast<const unsigned char*>(a.k_new);
+  const unsigned char* __restrict__ vn = reinterpret_cast<const unsigned char*>(a.v_new);
+  unsigned char* __restrict__ kp = reinterpret_cast<unsigned char*>(a.k_pool);
+  unsigned char* __restrict__ vp = reinterpret_cast<unsigned char*>(a.v_pool);
+  const size_t block_bytes = (size_t)kPageSize * a.head_bytes;
+#pragma unroll 4
+  for (int x = tid; x < rows * row_chunks; x += kThreads) {
+    const int i = x / row_chunks;
+    const int w = x % row_chunks;
+    const unsigned long long own = s_owner[i];
+    if (own == 0ull) continue;   // no request owns the row
+    const int r = (int)(own >> 32) - 1;
+    const int pos = (int)(own & 0xFFFFFFFFull);
+    const int pg = pos / kPageSize;
+    if (pg >= a.max_pages_per_seq) continue;
+    const int id = a.page_table[(size_t)r * a.max_pages_per_seq + pg];
+    if (id < 0 || id >= a.num_pages) continue;
+    const int h = w / head_chunks;
+    const int c = w % head_chunks;
+    const size_t src = ((size_t)(x0 + i) * a.num_kv_heads + h) * a.head_bytes + (size_t)c * 16;
+    const size_t dst = ((size_t)id * a.num_kv_heads + h) * block_bytes +
+                       (size_t)(pos % kPageSize) * a.head_bytes + (size_t)c * 16;
+    *reinterpret_cast<uint4*>(kp + dst) = *reinterpret_cast<const uint4*>(kn + src);
+    *reinterpret_cast<uint4*>(vp + dst) = *reinterpret_cast<const uint4*>(vn + src);
+  }
+}
+
 // Copy whole pages (every KV head, K and V) from src[i] to dst[i]: the device
 // half of a copy on write, when a request about to write into a shared page
 // takes a private copy of it first.  One workgroup per (pair, slice of the
@@ -124,9 +186,17 @@ hipError_t launch_copy_pages(const CopyPagesArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
+  if (a.head_bytes % 16 != 0) return hipErrorInvalidValue;
+  if (a.q_starts != nullptr && a.num_seqs <= kThreads) {
+    const long long grid = (a.total_rows + kRowsPerWg - 1) / kRowsPerWg;
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(append_flat_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+  }
   const long long grid = (long long)a.num_seqs * a.tiles_per_seq;
   if (grid <= 0) return hipSuccess;
-  if (grid > 0x7FFFFFFFLL || a.head_bytes % 16 != 0) return hipErrorInvalidValue;
+  if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(append_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }

@@ -160,7 +160,8 @@ struct AppendArgs {
   const int32_t* q_starts;  // [B+1] or null (derived on the device)
   int32_t num_seqs, num_kv_heads, max_pages_per_seq, num_pages;
   int32_t head_bytes;       // d * element size (a multiple of 16)
-  int32_t tiles_per_seq;    // row groups per request in the grid
+  int32_t tiles_per_seq;    // row groups per request in the per-request grid
+  int64_t total_rows;       // rows of k_new / v_new
 };
 
 int append_rows_per_wg();

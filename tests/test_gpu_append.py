@@ -56,15 +56,19 @@ def test_append_matches_oracle_bit_exact(Hkv, d, dtype, with_starts):
     assert np.array_equal(gv.view(np.uint8), ev.view(np.uint8))
 
 
-def test_append_skips_rows_whose_page_is_out_of_range():
+@pytest.mark.parametrize("with_starts", [False, True])
+def test_append_skips_rows_whose_page_is_out_of_range(with_starts):
     b, kn, vn = append_case(77, [40, 20], [8, 0], 2, 64, W.BF16)
+    print(f"case append bad page ids q_starts={with_starts}", flush=True)
     dev = device_batch(b)
     bad = dev["page_table"].clone()
     bad[0, 1] = b.num_pages + 5          # positions 16..31 of request 0
     bad[1, 0] = -1                       # positions 0..15 of request 1
     before_k, before_v = raw(dev["k_pool"]).copy(), raw(dev["v_pool"]).copy()
+    qs = torch.from_numpy(b.q_row_starts.astype(np.int32)).cuda() if with_starts else None
     pa.pa_append_kv(to_torch(kn, W.BF16), to_torch(vn, W.BF16), dev["k_pool"], dev["v_pool"], bad,
-                    dev["seq_lens"], dev["q_offsets"], max_seq_len=b.max_seq_len, max_q_len=b.max_q_len)
+                    dev["seq_lens"], dev["q_offsets"], q_starts=qs, max_seq_len=b.max_seq_len,
+                    max_q_len=b.max_q_len)
     torch.cuda.synchronize()
     # the oracle on the same table, with the bad rows' pages pointed at a scratch pool row
     tab = b.page_table.copy()
@@ -76,11 +80,13 @@ def test_append_skips_rows_whose_page_is_out_of_range():
     assert np.array_equal(raw(dev["v_pool"]).view(np.uint8), ev[:-1].view(np.uint8))
 
 
-def test_append_skips_a_request_with_a_negative_offset():
+@pytest.mark.parametrize("with_starts", [False, True])
+def test_append_skips_a_request_with_a_negative_offset(with_starts):
     # a negative q_offset breaks the contract (pa_validate_metadata reports
     # it); the kernel must then skip that request rather than write before
     # its first page
     b, kn, vn = append_case(78, [40, 20], [8, 0], 2, 64, W.BF16)
+    print(f"case append negative offset q_starts={with_starts}", flush=True)
     dev = device_batch(b)
     before_k, before_v = raw(dev["k_pool"]).copy(), raw(dev["v_pool"]).copy()
     offs = dev["q_offsets"].clone()
@@ -91,13 +97,60 @@ def test_append_skips_a_request_with_a_negative_offset():
                           kn[32:]])
     vn2 = np.concatenate([W.f32_to_bf16_bits(rng.standard_normal((rows0, 2, 64)).astype(np.float32)),
                           vn[32:]])
+    # request 0's claimed rows come first, so request 1's rows start at 44
+    qs = torch.tensor([0, rows0, rows0 + 20], dtype=torch.int32, device="cuda") if with_starts else None
     pa.pa_append_kv(to_torch(kn2, W.BF16), to_torch(vn2, W.BF16), dev["k_pool"], dev["v_pool"],
-                    dev["page_table"], dev["seq_lens"], offs, max_seq_len=b.max_seq_len,
+                    dev["page_table"], dev["seq_lens"], offs, q_starts=qs, max_seq_len=b.max_seq_len,
                     max_q_len=b.max_seq_len)   # a valid host bound the device offsets break
     torch.cuda.synchronize()
     # expected: request 1 appended, request 0 and everything else untouched
     ek, ev = ORACLE.append_kv(before_k, before_v, b.page_table[1:], b.seq_lens[1:], b.q_offsets[1:],
                               kn[32:], vn[32:])
+    assert np.array_equal(raw(dev["k_pool"]).view(np.uint8), ek.view(np.uint8))
+    assert np.array_equal(raw(dev["v_pool"]).view(np.uint8), ev.view(np.uint8))
+
+
+def test_append_with_an_empty_request_between_others():
+    # request 2 appends no row this step (q_offsets == seq_lens): the rows
+    # after it belong to request 3, on either launch shape
+    b, _, _ = append_case(79, [37, 300, 51, 129], [0, 170, 50, 128], 4, 128, W.BF16)
+    offs = b.q_offsets.copy()
+    offs[2] = b.seq_lens[2]
+    n = (b.seq_lens - offs).astype(np.int64)
+    rng = np.random.default_rng(80)
+    kn = W.f32_to_bf16_bits(rng.standard_normal((int(n.sum()), 4, 128)).astype(np.float32))
+    vn = W.f32_to_bf16_bits(rng.standard_normal((int(n.sum()), 4, 128)).astype(np.float32))
+    ek, ev = ORACLE.append_kv(b.k_pool, b.v_pool, b.page_table, b.seq_lens, offs, kn, vn)
+    for with_starts in (False, True):
+        print(f"case append empty request q_starts={with_starts}", flush=True)
+        dev = device_batch(b)
+        qs = (torch.from_numpy(np.concatenate([[0], np.cumsum(n)]).astype(np.int32)).cuda()
+              if with_starts else None)
+        pa.pa_append_kv(to_torch(kn, W.BF16), to_torch(vn, W.BF16), dev["k_pool"], dev["v_pool"],
+                        dev["page_table"], dev["seq_lens"], torch.from_numpy(offs).cuda(), q_starts=qs,
+                        max_seq_len=b.max_seq_len, max_q_len=b.max_q_len)
+        torch.cuda.synchronize()
+        assert np.array_equal(raw(dev["k_pool"]).view(np.uint8), ek.view(np.uint8))
+        assert np.array_equal(raw(dev["v_pool"]).view(np.uint8), ev.view(np.uint8))
+
+
+@pytest.mark.parametrize("B", [256, 300])
+def test_append_many_requests_with_row_starts(B):
+    # decode-like steps (one or a few rows per request) with q_starts: up to
+    # 256 requests take the launch over the step's rows, more take one
+    # workgroup per request
+    rng = np.random.default_rng(81 + B)
+    L = rng.integers(2, 200, size=B).astype(np.int32)
+    n = np.minimum(L, rng.integers(1, 4, size=B)).astype(np.int32)
+    b, kn, vn = append_case(82 + B, L, L - n, 2, 64, W.BF16)
+    print(f"case append B={B} rows={int(b.total_q)} q_starts=True", flush=True)
+    dev = device_batch(b)
+    qs = torch.from_numpy(b.q_row_starts.astype(np.int32)).cuda()
+    pa.pa_append_kv(to_torch(kn, W.BF16), to_torch(vn, W.BF16), dev["k_pool"], dev["v_pool"],
+                    dev["page_table"], dev["seq_lens"], dev["q_offsets"], q_starts=qs,
+                    max_seq_len=b.max_seq_len, max_q_len=b.max_q_len)
+    torch.cuda.synchronize()
+    ek, ev = ORACLE.append_kv(b.k_pool, b.v_pool, b.page_table, b.seq_lens, b.q_offsets, kn, vn)
     assert np.array_equal(raw(dev["k_pool"]).view(np.uint8), ek.view(np.uint8))
     assert np.array_equal(raw(dev["v_pool"]).view(np.uint8), ev.view(np.uint8))
 
