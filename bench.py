@@ -569,7 +569,7 @@ def main():
     kernels["append"] = {"bound": "hbm", "achieved": round(ap_gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(ap_gbs / HBM_PEAK_GBS, 4),
                          "traffic": load_traffic("append", source_hash("append.hip")),
-                         "ms": round(ap_ms, 4), "kernel": "append_kernel",
+                         "ms": round(ap_ms, 4), "kernel": "append_flat_kernel",
                          "work": ap_bytes, "work_unit": "B"}
     dominant = "prefill" if pf_ms >= dc_ms else "decode"
     roof = {k: kernels[dominant][k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
