@@ -51,7 +51,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0,
                     help="wall-clock budget of the oracle's CPU baseline sample")
-    ap.add_argument("--mode", choices=("step", "copy", "baselines", "configs"), default="step",
+    ap.add_argument("--mode", choices=("step", "copy", "baselines", "configs", "ceiling"), default="step",
                     help="step: the benchmark; copy: calibration of the HBM counters and "
                          "the streaming ceiling (a plain 1 GiB device copy and a read-only "
                          "reduction of known size); baselines: the Qwen3-4B-shaped decode "
@@ -59,7 +59,9 @@ def parse():
                          "pages and over a dense cache, and direct (non-flash) paged "
                          "attention; configs: one JSON line per named config and route "
                          "(cache-flushed per-call times, rate against peak, error against "
-                         "the oracle on sampled requests)")
+                         "the oracle on sampled requests); ceiling: the read rate of the "
+                         "decode route's access pattern (pa_read_blocks over 2 GiB in 4 KiB "
+                         "blocks, random order and in order, and 32 KiB blocks)")
     return ap.parse_args()
 
 
@@ -88,6 +90,41 @@ def copy_calibration(steps: int):
         us = e0.elapsed_time(e1) * 1e3 / steps
         res[name] = {"us": round(us, 2), "GB/s": round(nbytes / us / 1e3, 1), "bytes": nbytes}
     print(json.dumps({"calibration": res}), flush=True)
+
+
+def read_reference(steps: int = 20, warmup: int = 3) -> dict:
+    """The read rate the decode route's access pattern reaches on this
+    device: pa_read_blocks over 2 GiB (far past the 256 MB last-level cache)
+    in 4 KiB blocks -- one (page, KV head) K or V block at d = 128 in bf16 --
+    in a random order and in order, and in 32 KiB blocks (a page's K for 8 KV
+    heads) in a random order; each with HIP events on the launch stream."""
+    import torch
+    import paged_kv_cache_02_amd as pa
+    nbytes = 2 << 30
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    rng = np.random.default_rng(0)
+    res = {}
+    for name, bb, shuffle in (("4KiB_random", 4096, True), ("4KiB_in_order", 4096, False),
+                              ("32KiB_random", 32768, True)):
+        order = np.arange(nbytes // bb, dtype=np.int32)
+        if shuffle:
+            rng.shuffle(order)
+        call = pa.bind_read_blocks(buf, torch.from_numpy(order).cuda(), bb, sink)
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        res[name] = {"us": round(us, 1), "GB/s": round(nbytes / us / 1e3, 1)}
+    del buf
+    torch.cuda.empty_cache()
+    return res
 
 
 def baselines(steps: int, warmup: int):
@@ -402,6 +439,9 @@ def main():
     if args.mode == "copy":
         copy_calibration(args.steps)
         return
+    if args.mode == "ceiling":
+        print(json.dumps({"read_reference": read_reference(max(args.steps, 5), args.warmup)}), flush=True)
+        return
     if args.mode == "baselines":
         baselines(args.steps, args.warmup)
         return
@@ -603,6 +643,17 @@ def main():
         "single_launch": single,
         "roofline": roof,
         "cpu_baseline": None,
+    }
+    # after the timed region: the rate of the decode route's read pattern on
+    # this device (random 4 KiB blocks), against which the route's GB/s is
+    # also given
+    ref = read_reference()
+    result["hbm_read_reference"] = {
+        "pattern": "pa_read_blocks: 2 GiB in 4 KiB blocks (one (page, KV head) K or V block), random order, "
+                   "nontemporal 16-byte loads",
+        "GB/s": ref["4KiB_random"]["GB/s"],
+        "decode_frac": round(dec_gbs / ref["4KiB_random"]["GB/s"], 4),
+        "all": ref,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(full, args.cpu_budget_s)

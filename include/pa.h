@@ -361,6 +361,22 @@ pa_status pa_gather_kv(const pa_desc* desc, const void* k_pool, const void* v_po
                        const int32_t* page_table, int32_t req, int32_t seq_len, void* k_out,
                        void* v_out, void* stream);
 
+/* Measurement hook (not part of the attention path): the read rate of the
+ * decode kernels' access pattern.  Reads nblocks blocks of block_bytes
+ * (4096, 8192, 16384 or 32768) from buf (device, buf_blocks blocks, 16-byte
+ * aligned), block j at byte offset order[j] * block_bytes (order: int32
+ * device array; ids outside [0, buf_blocks) are skipped), with the loads
+ * the decode kernels use for K and V (16 bytes per lane, nontemporal), and
+ * XORs every 32-bit word read into *sink (device uint32; the caller zeroes
+ * it).  A (page, KV head) K or V block is P * d * 2 = 4096 bytes at d = 128
+ * in bf16, so 4096-byte blocks in a random order are what the decode route
+ * reads: decode is bound by these reads ("tiny-llm source reading", section
+ * "KV Cache changes the shape of the computation"), and its rate is
+ * measured against this one as well as against the device's peak.
+ * PA_ERR_ARG for a bad size or null pointer. */
+pa_status pa_read_blocks(const void* buf, int64_t buf_blocks, const int32_t* order, int32_t nblocks,
+                         int32_t block_bytes, uint32_t* sink, void* stream);
+
 /* Debugging aid: copies the metadata to the host (synchronizing `stream`)
  * and checks the device-array contract above (the page table, context
  * lengths and offsets of the "Paged KV Cache" section of the tiny-llm

@@ -63,6 +63,7 @@ _SIGS = {
     "pa_merge_partials": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                          ctypes.c_int32, _P, _P, _P, ctypes.c_int32, _P, _P]),
     "pa_gather_kv": (ctypes.c_int, [_D, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]),
+    "pa_read_blocks": (ctypes.c_int, [_P, ctypes.c_int64, _P, ctypes.c_int32, ctypes.c_int32, _P, _P]),
     "pa_validate_metadata": (ctypes.c_int, [_D, _P, _P, _P, _P]),
     "pa_append_kv": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "pa_pool_create": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p)]),
@@ -373,6 +374,23 @@ def pa_gather_kv(k_pool, v_pool, page_table, req, seq_len, *, desc=None, seq_len
     return k_out, v_out
 
 
+def pa_read_blocks(buf, order, block_bytes, sink):
+    """Read the blocks of the uint8 device tensor buf (block_bytes each) in
+    the order of the int32 device tensor order, XOR-folding every word into
+    the int32 device tensor sink (one element, zeroed by the caller): the
+    decode kernels' K/V read pattern on its own, for timing."""
+    _check(lib().pa_read_blocks(_ptr(buf), int(buf.numel()) // int(block_bytes), _ptr(order),
+                                int(order.numel()), int(block_bytes), _ptr(sink), _stream(buf.device)),
+           "pa_read_blocks")
+
+
+def bind_read_blocks(buf, order, block_bytes, sink) -> BoundCall:
+    """pa_read_blocks with fixed arguments (see BoundCall)."""
+    keep = (buf, order, sink)
+    return BoundCall("pa_read_blocks", keep, _ptr(buf), int(buf.numel()) // int(block_bytes), _ptr(order),
+                     int(order.numel()), int(block_bytes), _ptr(sink), _stream(buf.device))
+
+
 def pa_validate_metadata(desc: pa_desc, page_table, seq_lens, q_offsets=None) -> int:
     """Returns the status code (PA_OK or PA_ERR_METADATA); synchronizes."""
     return int(lib().pa_validate_metadata(ctypes.byref(desc), _ptr(page_table), _ptr(seq_lens),
@@ -491,7 +509,7 @@ class PagePool:
 
 __all__ = ["pa_desc", "pa_plan_info", "PaError", "lib", "make_desc", "pa_plan",
            "pa_workspace_bytes", "pa_decode", "pa_split_merge", "pa_prefill_chunk",
-           "pa_merge_partials", "pa_gather_kv", "pa_validate_metadata", "pa_status_str",
+           "pa_merge_partials", "pa_gather_kv", "pa_read_blocks", "bind_read_blocks", "pa_validate_metadata", "pa_status_str",
            "split_partials_view", "pa_append_kv", "bind_append_kv", "PagePool", "BoundCall",
            "bind_decode", "bind_prefill_chunk", "pa_copy_pages", "pa_decode_dense",
            "pa_decode_direct", "pa_mixed_attention", "bind_mixed_attention", "EXPORTED"]

@@ -671,6 +671,23 @@ pa_status pa_gather_kv(const pa_desc* d, const void* k_pool, const void* v_pool,
                                                                                      : PA_ERR_HIP;
 }
 
+pa_status pa_read_blocks(const void* buf, int64_t buf_blocks, const int32_t* order, int32_t nblocks,
+                         int32_t block_bytes, uint32_t* sink, void* stream) {
+  if (!buf || !order || !sink || buf_blocks < 0 || nblocks < 0 || !aligned16(buf) || !aligned4(order) ||
+      !aligned4(sink))
+    return PA_ERR_ARG;
+  if (!(block_bytes == 4096 || block_bytes == 8192 || block_bytes == 16384 || block_bytes == 32768))
+    return PA_ERR_ARG;
+  pa::ReadBlocksArgs a;
+  a.buf = buf;
+  a.order = order;
+  a.sink = sink;
+  a.buf_blocks = buf_blocks;
+  a.nblocks = nblocks;
+  a.block_bytes = block_bytes;
+  return pa::launch_read_blocks(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 pa_status pa_validate_metadata(const pa_desc* d, const int32_t* page_table,
                                const int32_t* seq_lens, const int32_t* q_offsets, void* stream) {
   pa_status st = check_desc(d);

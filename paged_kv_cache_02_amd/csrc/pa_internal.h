@@ -195,4 +195,18 @@ struct GatherArgs {
 
 hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
 
+// ---------------------------------------------------------------------------
+// read-bandwidth reference (measurement hook)
+// ---------------------------------------------------------------------------
+struct ReadBlocksArgs {
+  const void* buf;          // buf_blocks blocks of block_bytes
+  const int32_t* order;     // [nblocks] block ids; ids outside [0, buf_blocks) are skipped
+  uint32_t* sink;           // XOR of every word read
+  int64_t buf_blocks;
+  int32_t nblocks, block_bytes;
+};
+
+constexpr int kReadBlocksGrid = 2048;   // workgroups of the read-bandwidth reference
+hipError_t launch_read_blocks(const ReadBlocksArgs& a, hipStream_t s);
+
 }  // namespace pa

@@ -113,6 +113,10 @@ hipError_t launch_gather(const GatherArgs&, hipStream_t) {
   ++g_launches;
   return hipSuccess;
 }
+hipError_t launch_read_blocks(const ReadBlocksArgs&, hipStream_t) {
+  ++g_launches;
+  return hipSuccess;
+}
 }  // namespace pa
 
 // ---------------------------------------------------------------------------
@@ -284,6 +288,23 @@ static int asan_mode() {
     for (int r = 0; r < ROWS; ++r) CHECK(pa_pool_release(p, rows.data() + r * MP, MP, len[r], 16) == PA_OK);
     CHECK(pa_pool_num_free(p) == NP);
     pa_pool_destroy(p);
+  }
+  // ---- pa_read_blocks: argument checks
+  {
+    alignas(16) static unsigned char blk[4096];
+    int32_t order[2] = {0, 5};
+    uint32_t sink = 0;
+    const int before = g_launches.load();
+    CHECK(pa_read_blocks(nullptr, 1, order, 2, 4096, &sink, nullptr) == PA_ERR_ARG);
+    CHECK(pa_read_blocks(blk, 1, nullptr, 2, 4096, &sink, nullptr) == PA_ERR_ARG);
+    CHECK(pa_read_blocks(blk, 1, order, 2, 4096, nullptr, nullptr) == PA_ERR_ARG);
+    CHECK(pa_read_blocks(blk + 4, 1, order, 2, 4096, &sink, nullptr) == PA_ERR_ARG);   // misaligned
+    CHECK(pa_read_blocks(blk, 1, order, 2, 2048, &sink, nullptr) == PA_ERR_ARG);       // size
+    CHECK(pa_read_blocks(blk, -1, order, 2, 4096, &sink, nullptr) == PA_ERR_ARG);
+    CHECK(pa_read_blocks(blk, 1, order, -1, 4096, &sink, nullptr) == PA_ERR_ARG);
+    CHECK(g_launches.load() == before);
+    CHECK(pa_read_blocks(blk, 1, order, 2, 4096, &sink, nullptr) == PA_OK);
+    CHECK(g_launches.load() == before + 1);
   }
   std::printf("asan mode ok (%d launches stubbed)\n", g_launches.load());
   return 0;
