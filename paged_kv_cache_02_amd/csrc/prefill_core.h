@@ -507,36 +507,34 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
                           __attribute__((always_inline)) {
     if (kb > pos_hi) return;   // no key of the tile is visible to any row of this wave
     // ---- S^T = K Q^T: 2 key blocks x 2 row blocks ----
-    // The two key blocks' MFMA chains alternate (k-step s of block 0, then
-    // of block 1), so consecutive MFMAs never depend on each other; within a
-    // block the k-steps still accumulate in order.  Operand t (k-step t / 2
-    // of block t % 2) goes through a ring of kKSteps registers: the first
-    // kKSteps are requested before any MFMA, and each register is refilled
-    // with operand t + kKSteps as soon as MFMA t has been issued, so the
-    // MFMAs never wait on one LDS round trip each.
+    // All 8 K operands of a key block are requested before its MFMAs, and
+    // each register is refilled with the next block's operand as soon as its
+    // MFMA has been issued, so the MFMAs never wait on one LDS round trip
+    // each.
     static_assert(kRB == 1, "the operand pipeline below is written for one row block");
-    constexpr int kOps = 2 * GE::kKSteps;
-    auto kread = [&](int t) {
-      return *reinterpret_cast<const uint4*>(kst + (kaddr[t / 2] - kKBias) + (t % 2) * kKeyBlockBytes);
-    };
     floatx16_t sacc[kRB][2];
     uint4 ka[GE::kKSteps];
 #pragma unroll
-    for (int t = 0; t < GE::kKSteps; ++t) ka[t] = kread(t);
+    for (int s = 0; s < GE::kKSteps; ++s)
+      ka[s] = *reinterpret_cast<const uint4*>(kst + (kaddr[s] - kKBias));
 #pragma unroll
-    for (int t = 0; t < kOps; ++t) {
-      const int s = t / 2;
-      const int blk = t % 2;
+    for (int s = 0; s < GE::kKSteps; ++s) {
       const floatx16_t zero = {};
-      sacc[0][blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[t % GE::kKSteps]), as_bf16x8(qv[0][s]),
-                                                             s == 0 ? zero : sacc[0][blk], 0, 0, 0);
-      if (t + GE::kKSteps < kOps) ka[t % GE::kKSteps] = kread(t + GE::kKSteps);
+      sacc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[s]), as_bf16x8(qv[0][s]),
+                                                           s == 0 ? zero : sacc[0][0], 0, 0, 0);
+      ka[s] = *reinterpret_cast<const uint4*>(kst + (kaddr[s] - kKBias + kKeyBlockBytes));
     }
-    // schedule: the first kKSteps reads, then each MFMA followed by the read
-    // that refills its operand register, then the last kKSteps MFMAs
+#pragma unroll
+    for (int s = 0; s < GE::kKSteps; ++s) {
+      const floatx16_t zero = {};
+      sacc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[s]), as_bf16x8(qv[0][s]),
+                                                           s == 0 ? zero : sacc[0][1], 0, 0, 0);
+    }
+    // schedule: the first block's reads, then each MFMA followed by the read
+    // that refills its operand register, then the second block's MFMAs
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, GE::kKSteps, 0);
 #pragma unroll
-    for (int t = 0; t < kOps - GE::kKSteps; ++t) {
+    for (int s = 0; s < GE::kKSteps; ++s) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
     }
