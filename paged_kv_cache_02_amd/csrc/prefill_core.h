@@ -65,6 +65,7 @@ constexpr int kTileRows = kWavesPerGroup * kRowsPerWave;  // packed (token, head
 constexpr int kTileKeys = 64;                     // keys per KV tile (4 pages)
 constexpr int kPagesPerTile = kTileKeys / kPageSize;
 constexpr int kLdsPages = 2048;                   // page ids kept in LDS
+constexpr int kSpecTiles = 64;                    // tiles whose page ids are read ahead (one per lane)
 constexpr float kRescaleLog2 = 8.0f;
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -169,10 +170,10 @@ struct TileGeo {
   int L, o, n, rows_total, row_base, kmax, ntiles;
 };
 
-__device__ __forceinline__ TileGeo tile_geo(const PrefillArgs& a, int r, int t, int group) {
+__device__ __forceinline__ TileGeo tile_geo_of(int L, int o, int t, int group) {
   TileGeo tg;
-  tg.L = a.seq_lens[r];
-  tg.o = a.q_offsets[r];
+  tg.L = L;
+  tg.o = o;
   tg.n = tg.L - tg.o;
   tg.rows_total = tg.n * group;
   tg.row_base = t * kTileRows;
@@ -180,6 +181,10 @@ __device__ __forceinline__ TileGeo tile_geo(const PrefillArgs& a, int r, int t, 
   tg.kmax = tg.o + last_row / group + 1;   // keys the tile's last row sees
   tg.ntiles = (tg.kmax + kTileKeys - 1) / kTileKeys;
   return tg;
+}
+
+__device__ __forceinline__ TileGeo tile_geo(const PrefillArgs& a, int r, int t, int group) {
+  return tile_geo_of(a.seq_lens[r], a.q_offsets[r], t, group);
 }
 
 __device__ __forceinline__ int num_splits_of(int ntiles, int kv_tiles_per_split) {
@@ -340,6 +345,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
   __shared__ __align__(1024) unsigned char k_b0[GE::kTileBytes];
   __shared__ __align__(1024) unsigned char k_b1[GE::kTileBytes];
   __shared__ int s_pages[kLdsPages];
+  __shared__ int s_spec[kWaves][kSpecTiles];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -353,13 +359,32 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
   const int T = a.tiles_per_seq;
   const int S = a.num_splits;
 
-  const TileGeo tg = tile_geo(a, r, t, group);
+  // Lane j of each wave copies entry 4j + wave of the request's table row
+  // (the page this wave moves for KV tile j) into the wave's row of s_spec,
+  // by DMA, while the request's lengths are read: once the tile geometry
+  // says which tile the wave's group starts at, its page id is one LDS read
+  // away, and the first tile's copy waits for one memory round trip after
+  // the lengths instead of two.  Groups starting past kSpecTiles read the
+  // entry itself.
+  // (the request's lengths and first row are requested before the DMA, as
+  // scalar loads, so waiting for them never waits for the copies below)
+  const int req_L = a.seq_lens[r];
+  const int req_o = a.q_offsets[r];
+  const int req_q0 = a.q_starts != nullptr ? a.q_starts[r] : 0;
+  const int32_t* __restrict__ ptab = a.page_table + (size_t)r * a.max_pages_per_seq;
+  {
+    const int lp = kPagesPerTile * lane + wave;
+    __builtin_amdgcn_global_load_lds(ptab + (lp < a.max_pages_per_seq ? lp : a.max_pages_per_seq - 1),
+                                     (lds_void*)&s_spec[wave_id][0], 4, 0, 0);
+  }
+
+  const TileGeo tg = tile_geo_of(req_L, req_o, t, group);
   if (tg.n <= 0 || tg.row_base >= tg.rows_total) return;
   const int nsp = num_splits_of(tg.ntiles, a.kv_tiles_per_split);
   if (split >= nsp) return;
   const int kt0 = split * a.kv_tiles_per_split;
   const int kt1 = min(kt0 + a.kv_tiles_per_split, tg.ntiles);
-  const int q_start = q_start_of(a, r, lane);
+  const int q_start = a.q_starts != nullptr ? req_q0 : q_start_of(a, r, lane);
 
   // this lane's query row (one 32-row block per wave)
   const int Hq = a.num_q_heads;
@@ -386,7 +411,6 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
 
   const __bf16* __restrict__ kpool = reinterpret_cast<const __bf16*>(a.k_pool);
   const __bf16* __restrict__ vpool = reinterpret_cast<const __bf16*>(a.v_pool);
-  const int32_t* __restrict__ ptab = a.page_table + (size_t)r * a.max_pages_per_seq;
   const int npages = min((tg.kmax + kPageSize - 1) / kPageSize, a.max_pages_per_seq);
 
   PageIds pi;
@@ -399,10 +423,26 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
   // own copies overwrite first (rows 0-15 in the K slice, 16-31 in the V
   // slice), laid out like K rows (16-byte chunks XOR-swizzled by row).  They
   // are read into registers after the first barrier and waited for before
-  // this wave's first copy into stage 1, so no other wave is involved.  The
-  // group's first tile's page id is read straight from the table here too,
-  // so both reads are in flight with the page-id copy below (the raw entry
-  // is clamped only where it is used).
+  // this wave's first copy into stage 1, so no other wave is involved.  They
+  // are requested after the group's first tile (whose page id comes from
+  // s_spec), and the page-id copy below after both, so all three are in
+  // flight together.
+  const int mid = kt0 + (kt1 - kt0 + 1) / 2;
+  const int first_kt = grp == 0 ? kt0 : mid;
+  const int first_lp = first_kt * kPagesPerTile + wave;
+  const bool first_valid = first_kt < (grp == 0 ? mid : kt1) && first_lp < npages;
+  const int L = tg.L;
+  // the group's first tile into stage 0 (K by DMA, V into registers)
+  VRegs<D> vr;
+  if (first_kt < (grp == 0 ? mid : kt1)) {
+    int id = -1;
+    if (first_valid) {
+      id = first_kt < kSpecTiles ? s_spec[wave_id][first_kt] : ptab[first_lp];
+      id = __builtin_amdgcn_readfirstlane(id);
+      id = id < 0 ? 0 : (id >= a.num_pages ? a.num_pages - 1 : id);
+    }
+    load_tile<D>(grp == 0 ? k_a0 : k_b0, vr, kpool, vpool, id, first_kt, L, Hkv, g, wave, lane);
+  }
   constexpr int kSlice = (GE::kDmaPerTile / kWavesPerGroup) * 1024;   // a wave's part of a stage
   static_assert(16 * GE::kRowBytes == kSlice, "16 query rows fill a wave's slice");
   unsigned char* const qk = (grp == 0 ? k_a1 : k_b1) + wave * kSlice;
@@ -432,11 +472,6 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
   } else {
     load_q_rows([&](int rho) { return rho / group; });
   }
-  const int mid = kt0 + (kt1 - kt0 + 1) / 2;
-  const int first_kt = grp == 0 ? kt0 : mid;
-  const int first_lp = first_kt * kPagesPerTile + wave;
-  const bool first_valid = first_kt < (grp == 0 ? mid : kt1) && first_lp < npages;
-  const int first_raw = first_valid ? ptab[first_lp] : -1;
 
   const int p0 = kt0 * kPagesPerTile;
   const int p1 = min(kt1 * kPagesPerTile, npages);
@@ -647,7 +682,6 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
   // one LDS stage while tile i+1 is copied into the other by DMA; a barrier
   // per step (shared by both groups, which run the same number of steps)
   // hands stages over.  Unrolled by two so each step names its stages.
-  const int L = tg.L;
   const int nloop = mid - kt0;
   auto run = [&](auto gtag) __attribute__((always_inline)) {
     constexpr int GRP = decltype(gtag)::value;
@@ -660,16 +694,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
     // The page this wave moves for the next tile is looked up one step
     // ahead (an LDS read whose latency the step's compute hides).
     auto wave_page = [&](int kt) { return tile_page_lanes(pi, min(kt, my1 - 1), wave); };
-    VRegs<D> vr;
-    if (my0 < my1) {
-      int id = -1;
-      if (first_valid) {
-        id = __builtin_amdgcn_readfirstlane(first_raw);
-        id = id < 0 ? 0 : (id >= a.num_pages ? a.num_pages - 1 : id);
-      }
-      load_tile<D>(ks0, vr, kpool, vpool, id, my0, L, Hkv, g, wave, lane);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_waitcnt(0);   // the first tile (requested above), the query rows, the page ids
     if (my0 < my1) store_v<D>(vs0, vr, wave, lane);
     __syncthreads();   // stage 0, the query rows and the page ids in LDS
     {
