@@ -45,7 +45,9 @@
 // Keys at or past a row's position are masked by select before the max.  K
 // and V rows of keys at or past seq_len (page tails, possibly NaN) are never
 // loaded: their LDS slots are zero-filled, so no NaN meets a zero weight.
-// Page-table entries past the pages needed are never read.
+// Page-table entries past the pages needed are never used: the prologue's
+// read-ahead of the first tiles' entries stays inside the request's row and
+// takes an entry only for a tile the request has.
 #pragma once
 
 #include "pa_internal.h"
