@@ -361,15 +361,14 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
   const int T = a.tiles_per_seq;
   const int S = a.num_splits;
 
-  // Lane j of each wave copies entry 4j + wave of the request's table row
-  // (the page this wave moves for KV tile j) into the wave's row of s_spec,
-  // by DMA, while the request's lengths are read: once the tile geometry
-  // says which tile the wave's group starts at, its page id is one LDS read
-  // away, and the first tile's copy waits for one memory round trip after
-  // the lengths instead of two.  Groups starting past kSpecTiles read the
-  // entry itself.
-  // (the request's lengths and first row are requested before the DMA, as
-  // scalar loads, so waiting for them never waits for the copies below)
+  // The request's length, offset and first row are requested first (scalar
+  // loads, so waiting for them never waits for the copies below).  Beside
+  // them, lane j of each wave copies entry 4j + wave of the request's table
+  // row (the page this wave moves for KV tile j) into the wave's row of
+  // s_spec by DMA: once the tile geometry says which tile the wave's group
+  // starts at, its page id is one LDS read away, and the first tile's copy
+  // waits for one memory round trip after the lengths instead of two.
+  // Groups starting past kSpecTiles read the entry itself.
   const int req_L = a.seq_lens[r];
   const int req_o = a.q_offsets[r];
   const int req_q0 = a.q_starts != nullptr ? a.q_starts[r] : 0;
@@ -420,15 +419,6 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
   pi.npages = npages;
   pi.num_pages = a.num_pages;
   pi.lds = nullptr;
-  // The wave's 32 query rows come in by DMA, whole rows per instruction,
-  // into the slices of its group's stage-1 K and V buffers that this wave's
-  // own copies overwrite first (rows 0-15 in the K slice, 16-31 in the V
-  // slice), laid out like K rows (16-byte chunks XOR-swizzled by row).  They
-  // are read into registers after the first barrier and waited for before
-  // this wave's first copy into stage 1, so no other wave is involved.  They
-  // are requested after the group's first tile (whose page id comes from
-  // s_spec), and the page-id copy below after both, so all three are in
-  // flight together.
   const int mid = kt0 + (kt1 - kt0 + 1) / 2;
   const int first_kt = grp == 0 ? kt0 : mid;
   const int first_lp = first_kt * kPagesPerTile + wave;
@@ -445,6 +435,15 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
     }
     load_tile<D>(grp == 0 ? k_a0 : k_b0, vr, kpool, vpool, id, first_kt, L, Hkv, g, wave, lane);
   }
+  // The wave's 32 query rows come in by DMA, whole rows per instruction,
+  // into the slices of its group's stage-1 K and V buffers that this wave's
+  // own copies overwrite first (rows 0-15 in the K slice, 16-31 in the V
+  // slice), laid out like K rows (16-byte chunks XOR-swizzled by row).  They
+  // are read into registers after the first barrier and waited for before
+  // this wave's first copy into stage 1, so no other wave is involved.  They
+  // are requested after the group's first tile (whose page id comes from
+  // s_spec), and the page-id copy below after both, so all three are in
+  // flight together.
   constexpr int kSlice = (GE::kDmaPerTile / kWavesPerGroup) * 1024;   // a wave's part of a stage
   static_assert(16 * GE::kRowBytes == kSlice, "16 query rows fill a wave's slice");
   unsigned char* const qk = (grp == 0 ? k_a1 : k_b1) + wave * kSlice;
