@@ -209,6 +209,23 @@ def test_long_context_short_chunk_splits_across_workgroups():
     compare(b, out2, lse2, ro, rl, label="prefill unsplit")
 
 
+def test_groups_starting_past_the_read_ahead_tiles():
+    # a chunk at the end of a 9000-key context: the second wave group starts
+    # at KV tile 71, past the 64 tiles whose page ids the prologue reads
+    # ahead, so its first page id comes straight from the table; the split
+    # route's later splits start past tile 64 as well
+    b = chunk_batch(59, [9000, 1000], [8800, 900], 32, 8, 128, pool_factor=1.2)
+    dev = device_batch(b)
+    print("case prefill groups past the read-ahead tiles", flush=True)
+    ro, rl = oracle_run(b)
+    for split in (False, True):
+        out, lse = pa.pa_prefill_chunk(dev["q"], dev["k_pool"], dev["v_pool"], dev["page_table"],
+                                       dev["seq_lens"], dev["q_offsets"], b.scale, split=split,
+                                       max_seq_len=b.max_seq_len, max_q_len=b.max_q_len)
+        torch.cuda.synchronize()
+        compare(b, out, lse, ro, rl, label=f"prefill past the read-ahead tiles split={split}")
+
+
 def test_bound_call_matches_the_wrapper():
     b = chunk_batch(77, [600, 300, 129], [88, 0, 1], 32, 8, 128)
     dev = device_batch(b)
