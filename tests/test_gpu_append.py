@@ -36,7 +36,7 @@ def append_case(seed, lens, offs, Hkv, d, dtype, pool_factor=1.5):
 
 
 @pytest.mark.parametrize("Hkv,d,dtype", [(8, 128, W.BF16), (2, 64, W.BF16), (4, 128, W.F32),
-                                         (1, 64, W.F32), (8, 64, W.BF16)])
+                                         (1, 64, W.F32), (8, 64, W.BF16), (16, 128, W.F32)])
 @pytest.mark.parametrize("with_starts", [False, True])
 def test_append_matches_oracle_bit_exact(Hkv, d, dtype, with_starts):
     # prompt from 0, chunks crossing pages, one decode token, page-aligned chunk
