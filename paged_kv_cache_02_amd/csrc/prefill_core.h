@@ -379,10 +379,13 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
                                      (lds_void*)&s_spec[wave_id][0], 4, 0, 0);
   }
 
+  // a workgroup that leaves early first waits for its read-ahead copy, so
+  // no copy lands in LDS that the next workgroup on the CU already owns
+  auto leave = [&]() { __builtin_amdgcn_s_waitcnt(0); };
   const TileGeo tg = tile_geo_of(req_L, req_o, t, group);
-  if (tg.n <= 0 || tg.row_base >= tg.rows_total) return;
+  if (tg.n <= 0 || tg.row_base >= tg.rows_total) return leave();
   const int nsp = num_splits_of(tg.ntiles, a.kv_tiles_per_split);
-  if (split >= nsp) return;
+  if (split >= nsp) return leave();
   const int kt0 = split * a.kv_tiles_per_split;
   const int kt1 = min(kt0 + a.kv_tiles_per_split, tg.ntiles);
   const int q_start = a.q_starts != nullptr ? req_q0 : q_start_of(a, r, lane);
