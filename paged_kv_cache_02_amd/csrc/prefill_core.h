@@ -860,8 +860,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
 #pragma unroll
         for (int i = 0; i < kStores; ++i)
           if (orr[i] >= 0)
-            *reinterpret_cast<uint4*>(reinterpret_cast<__bf16*>(a.out) + (size_t)orr[i] * D + kKeep * 32 + cc * 8) =
-                x[i];
+            __builtin_nontemporal_store(
+                u32x4_t{x[i].x, x[i].y, x[i].z, x[i].w},
+                reinterpret_cast<u32x4_t*>(reinterpret_cast<__bf16*>(a.out) + (size_t)orr[i] * D + kKeep * 32 + cc * 8));
         if (GRP == 0 && a.lse != nullptr && half == 0 && row_valid[rb])
           a.lse[(size_t)(q_start + tok[rb]) * Hq + (size_t)g * group + hh[rb]] = lse;
       } else {
