@@ -8,8 +8,14 @@ from the fp32 weights, and the output rounded to bf16.  The only knob is how
 the weights enter the P V product: rounded to bf16 (8-bit significand), to
 fp16 (11 bits; the kernel's choice) or as a bf16 pair (high part plus
 remainder).  On rows dominated by a few values near 4 the bf16 weights move
-outputs past the 1e-2 bar; fp16 weights and the pair stay inside it.  CPU
-only; the GPU tests check the kernel itself on the same case."""
+outputs past the 1e-2 bar; fp16 weights and the pair stay inside it.
+
+A fourth form keeps bf16 weights but divides by the sum of the rounded
+weights (so the weights' rounding errors cancel against v - o instead of
+adding up): closer, still past the bar, because near |o| = 4 the output's
+own bf16 rounding takes up to 2^-7 of it and leaves about 2e-3 for the
+weights, which needs fp16's 11 bits.  CPU only; the GPU tests check the
+kernel itself on the same case."""
 import math
 
 import numpy as np
@@ -26,7 +32,7 @@ def bf16(x):
 
 
 def weights_as(p, mode):
-    if mode == "bf16":
+    if mode in ("bf16", "bf16_self"):
         return bf16(p).astype(np.float64)
     if mode == "f16":
         return p.astype(np.float16).astype(np.float64)
@@ -36,7 +42,9 @@ def weights_as(p, mode):
 
 def model_request(q, K, V, o, G, scale, mode):
     """One request's (KV head's) rows, packed token-major, as the kernel
-    forms them; returns bf16 outputs (as float64)."""
+    forms them; returns bf16 outputs (as float64).  Mode "bf16_self" rounds
+    the weights to bf16 and sums the rounded weights for the divisor; every
+    other mode sums the fp32 weights."""
     n, _, d = q.shape
     rows = n * G
     Q = q.reshape(rows, d).astype(np.float64)
@@ -69,6 +77,8 @@ def model_request(q, K, V, o, G, scale, mode):
                     m = np.where(need, mn, m)
                 mref = np.where(np.isneginf(m), 0, m).astype(np.float32)
                 p = np.where(vis, np.exp2((s * sl2 - mref[:, None]).astype(np.float32)), 0).astype(np.float32)
+                if mode == "bf16_self":
+                    p = bf16(p).astype(np.float32)
                 l = (l + p.sum(axis=1, dtype=np.float32)).astype(np.float32)
                 acc = acc + weights_as(p, mode) @ V[k0:k1].astype(np.float64)
             parts.append((m, l, acc))
@@ -113,8 +123,11 @@ def test_bf16_weights_cross_the_bar_where_fp16_weights_do_not(seed):
     e_bf16, omax = max_err(b, "bf16")
     e_f16, _ = max_err(b, "f16")
     e_pair, _ = max_err(b, "pair")
+    e_self, _ = max_err(b, "bf16_self")
     print(f"seed {seed}: max|out| {omax:.3f}; max|d out| bf16 {e_bf16:.4f}, fp16 {e_f16:.4f}, "
-          f"bf16 pair {e_pair:.4f}")
+          f"bf16 pair {e_pair:.4f}, bf16 over its own sum {e_self:.4f}")
     assert omax < 4.0                 # the range where the 1e-2 bar leaves room for one bf16 step
     assert e_bf16 > OUT_TOL           # one bf16 rounding of the weights is not enough
+    assert e_self > OUT_TOL           # ... even when the divisor sums the same rounded weights
+    assert e_self < e_bf16
     assert e_f16 <= OUT_TOL and e_pair <= OUT_TOL
