@@ -26,6 +26,12 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 ops are kept out of the generated code on purpose
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # kernarg preloading: a kernel's leading scalar and pointer arguments
+    # (up to the user-SGPR limit) arrive in SGPRs at wave launch instead of
+    # through a load of the kernel-argument segment; kernels whose first
+    # argument is a struct get none.  The compiler keeps a 256-byte entry
+    # that loads them for firmware without the feature.
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall", "-Wno-unused-function",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]

@@ -96,17 +96,23 @@ __global__ void __launch_bounds__(kThreads) append_kernel(AppendArgs a) {
 // the rows it owns with (r + 1, position); the largest r wins where
 // inconsistent metadata makes two requests claim a row.  Rows past total_q
 // are never touched, so no metadata can make this kernel read past k_new.
-__global__ void __launch_bounds__(kThreads) append_flat_kernel(AppendArgs a) {
+// The row starts, lengths, offsets and sizes come before the argument
+// struct as plain scalars and pointers (equal to the struct's fields of the
+// same names), so that the library's build preloads them into SGPRs at
+// launch and the owner scan's reads need no load of the kernel arguments.
+__global__ void __launch_bounds__(kThreads)
+append_flat_kernel(const int32_t* q_starts, const int32_t* seq_lens, const int32_t* q_offsets,
+                   int num_seqs, long long total_rows, AppendArgs a) {
   __shared__ unsigned long long s_owner[kRowsPerWg];
   const int tid = threadIdx.x;
   const long long x0 = (long long)blockIdx.x * kRowsPerWg;
-  const int rows = a.total_rows - x0 < kRowsPerWg ? (int)(a.total_rows - x0) : kRowsPerWg;
+  const int rows = total_rows - x0 < kRowsPerWg ? (int)(total_rows - x0) : kRowsPerWg;
   if (tid < kRowsPerWg) s_owner[tid] = 0ull;
   __syncthreads();
-  if (tid < a.num_seqs) {
-    const long long st = a.q_starts[tid];
-    const int L = a.seq_lens[tid];
-    const int o = a.q_offsets[tid];
+  if (tid < num_seqs) {
+    const long long st = q_starts[tid];
+    const int L = seq_lens[tid];
+    const int o = q_offsets[tid];
     const int n = L - o;
     if (o >= 0 && n > 0) {
       const long long lo = st > x0 ? st : x0;
@@ -191,7 +197,8 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
     const long long grid = (a.total_rows + kRowsPerWg - 1) / kRowsPerWg;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(append_flat_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(append_flat_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, a.q_starts,
+                       a.seq_lens, a.q_offsets, a.num_seqs, (long long)a.total_rows, a);
     return hipGetLastError();
   }
   const long long grid = (long long)a.num_seqs * a.tiles_per_seq;

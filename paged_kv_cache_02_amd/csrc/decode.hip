@@ -371,11 +371,18 @@ decode_balanced_kernel(DecodeArgs a, const int32_t* __restrict__ page_table,
 // are padding whose results are never written.
 // ---------------------------------------------------------------------------
 
+// The arguments the prologue needs first (the lengths, the batch and pool
+// sizes, the page table, the partial outputs) come before the argument
+// struct as plain scalars and pointers, so that the library's build
+// (kernarg preloading) hands them to the wave in SGPRs at launch: the first
+// length read goes out without waiting on a load of the kernel arguments,
+// whose other fields arrive while it is in flight.  They equal the struct's
+// fields of the same names.
 template <int D, int G>
 __global__ void __launch_bounds__(kThreads, 2)
-decode_mfma_kernel(DecodeArgs a, const int32_t* __restrict__ page_table,
-                   const int32_t* __restrict__ seq_lens, float* __restrict__ o_part,
-                   float* __restrict__ lse_part, int32_t* __restrict__ range_meta) {
+decode_mfma_kernel(const int32_t* __restrict__ seq_lens, int B, int maxp, int Hkv, int V,
+                   const int32_t* __restrict__ page_table, float* __restrict__ o_part,
+                   float* __restrict__ lse_part, int32_t* __restrict__ range_meta, DecodeArgs a) {
   using M = MShape<D>;
   static_assert(G <= 16, "at most 16 query heads per KV head");
   // pages whose K/V loads are in flight ahead of the one computed: with one
@@ -390,10 +397,6 @@ decode_mfma_kernel(DecodeArgs a, const int32_t* __restrict__ page_table,
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   const int Hq = a.num_q_heads;
-  const int Hkv = a.num_kv_heads;
-  const int B = a.num_seqs;
-  const int maxp = a.max_pages_per_seq;
-  const int V = a.num_splits;
   const int g = blockIdx.x % Hkv;
   const int v = (blockIdx.x / Hkv) * kWaves + wave;
   unsigned char* vslot = vslots[wave];
@@ -542,8 +545,9 @@ hipError_t launch_mfma_t(const DecodeArgs& a, hipStream_t s) {
   if (grid <= 0 || a.num_seqs <= 0) return hipSuccess;
   if (grid > 0x7FFFFFFFLL || a.num_splits % kWaves != 0 || a.num_seqs > kMaxBalancedSeqs)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL((decode_mfma_kernel<D, G>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, a.page_table,
-                     a.seq_lens, a.o_part, a.lse_part, a.range_meta);
+  hipLaunchKernelGGL((decode_mfma_kernel<D, G>), dim3((unsigned)grid), dim3(kThreads), 0, s, a.seq_lens,
+                     a.num_seqs, a.max_pages_per_seq, a.num_kv_heads, a.num_splits, a.page_table,
+                     a.o_part, a.lse_part, a.range_meta, a);
   return hipGetLastError();
 }
 

@@ -42,29 +42,36 @@ __device__ __forceinline__ __bf16 cast_out<__bf16>(float x) { return (__bf16)x; 
 template <>
 __device__ __forceinline__ float cast_out<float>(float x) { return x; }
 
+// The range table, the sizes and the partial arrays come before the
+// argument struct as plain scalars and pointers (equal to the struct's fields
+// of the same names), so that the library's build (kernarg preloading) hands
+// them to the wave in SGPRs at launch and the first read of the range table
+// does not wait on a load of the kernel arguments.
 template <typename T, int D>
-__global__ void __launch_bounds__(64 * kWavesPerBlock) merge_kernel(MergeArgs a) {
+__global__ void __launch_bounds__(64 * kWavesPerBlock)
+merge_kernel(const int32_t* __restrict__ range_meta, int rows, int heads, int num_splits,
+             const float* __restrict__ o_part, const float* __restrict__ lse_part, MergeArgs a) {
   const int lane = threadIdx.x & 63;
   const long long rh = (long long)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  const long long nrh = (long long)a.rows * a.heads;
+  const long long nrh = (long long)rows * heads;
   if (rh >= nrh) return;
   // partial s of this (row, head) is row  base + s * step  of the partial arrays
   long long base, step;
   int S;
-  if (a.range_meta == nullptr) {
-    S = a.num_splits;
+  if (range_meta == nullptr) {
+    S = num_splits;
     base = rh * S;
     step = 1;
   } else {
-    const long long r = rh / a.heads;
-    const int first = a.range_meta[2 * r];
-    const int last = a.range_meta[2 * r + 1];
+    const long long r = rh / heads;
+    const int first = range_meta[2 * r];
+    const int last = range_meta[2 * r + 1];
     S = last >= first ? last - first + 1 : 0;
-    base = (r + first) * a.heads + rh % a.heads;
-    step = a.heads;
+    base = (r + first) * heads + rh % heads;
+    step = heads;
   }
-  const float* lp = a.lse_part;
-  const float* op = a.o_part;
+  const float* lp = lse_part;
+  const float* op = o_part;
   constexpr int kPer = D / 64;
   constexpr int kBatch = 8;   // partial rows requested together
 
@@ -138,7 +145,7 @@ hipError_t launch_t(const MergeArgs& a, hipStream_t s) {
   const long long grid = (nrh + kWavesPerBlock - 1) / kWavesPerBlock;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((merge_kernel<T, D>), dim3((unsigned)grid), dim3(64 * kWavesPerBlock), 0, s,
-                     a);
+                     a.range_meta, a.rows, a.heads, a.num_splits, a.o_part, a.lse_part, a);
   return hipGetLastError();
 }
 

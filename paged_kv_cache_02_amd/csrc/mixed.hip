@@ -113,7 +113,7 @@ __global__ void __launch_bounds__(kThreads, 1) mixed_kernel(PrefillArgs a) {
   if (r < 0) return;
 
   if (prefill) {
-    pf::prefill_tile<D>(a, G, r, uniform(s_pick[1]), g, 0);
+    pf::prefill_tile<D>(a, pf::prefill_hot(a), G, r, uniform(s_pick[1]), g, 0);
     return;
   }
 

@@ -9,22 +9,27 @@ namespace {
 
 using namespace pf;
 
+// The grid decomposition and the values the tile reads first come before
+// the argument struct as plain scalars and pointers (equal to the struct's
+// fields of the same names), so that the library's build preloads them into
+// SGPRs at launch.
 template <int D>
-__global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a, int group) {
+__global__ void __launch_bounds__(kThreads, 1)
+prefill_kernel(const int32_t* seq_lens, const int32_t* q_offsets, const int32_t* q_starts,
+               const int32_t* page_table, int Hkv, int T, int S, int num_seqs, int maxp, int group,
+               PrefillArgs a) {
   // grid: KV head fastest (a (request, head) pair's tiles share an XCD when
   // Hkv is a multiple of 8), then split, then row tiles and requests in
   // reverse so the heavier tiles start first
-  const int Hkv = a.num_kv_heads;
-  const int T = a.tiles_per_seq;
-  const int S = a.num_splits;
   int bid = blockIdx.x;
   const int g = bid % Hkv;
   bid /= Hkv;
   const int split = bid % S;
   bid /= S;
   const int t = T - 1 - (bid % T);
-  const int r = a.num_seqs - 1 - bid / T;
-  prefill_tile<D>(a, group, r, t, g, split);
+  const int r = num_seqs - 1 - bid / T;
+  const PrefillHot h{seq_lens, q_offsets, q_starts, page_table, maxp};
+  prefill_tile<D>(a, h, group, r, t, g, split);
 }
 
 // Merge pass for split row tiles: one workgroup per (request, row tile, KV
@@ -88,7 +93,9 @@ hipError_t launch_d(const PrefillArgs& a, int group, hipStream_t s) {
   const long long grid = units * a.num_splits;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(prefill_kernel<D>, dim3((unsigned)grid), dim3(kThreads), 0, s, a, group);
+  hipLaunchKernelGGL(prefill_kernel<D>, dim3((unsigned)grid), dim3(kThreads), 0, s, a.seq_lens,
+                     a.q_offsets, a.q_starts, a.page_table, a.num_kv_heads, a.tiles_per_seq,
+                     a.num_splits, a.num_seqs, a.max_pages_per_seq, group, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_splits <= 1) return e;
   hipLaunchKernelGGL(prefill_merge_kernel<D>, dim3((unsigned)units), dim3(256), 0, s, a, group);

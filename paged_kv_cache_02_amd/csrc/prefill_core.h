@@ -325,12 +325,30 @@ template <int N>
 struct GroupTag {
   static constexpr int value = N;
 };
+// The fields of PrefillArgs that a row tile reads first (the request's
+// length, offset and first row, and its page-table row).  The prefill
+// kernel takes them as leading scalar arguments, which the library's build
+// preloads into SGPRs, so the first reads need no load of the kernel
+// arguments; the single launch copies them out of its argument struct.
+struct PrefillHot {
+  const int32_t* seq_lens;
+  const int32_t* q_offsets;
+  const int32_t* q_starts;
+  const int32_t* page_table;
+  int max_pages_per_seq;
+};
+
+__device__ __forceinline__ PrefillHot prefill_hot(const PrefillArgs& a) {
+  return PrefillHot{a.seq_lens, a.q_offsets, a.q_starts, a.page_table, a.max_pages_per_seq};
+}
+
 // Row tile t of request r for KV head g, key-range split `split` (0 when
 // unsplit): the whole workgroup of kThreads threads.  Writes the tile's rows
-// of out and lse, or the split's partial rows.
+// of out and lse, or the split's partial rows.  `h` holds the same values as
+// the corresponding fields of `a`.
 template <int D>
-__device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, int r, int t, int g,
-                                             int split) {
+__device__ __forceinline__ void prefill_tile(const PrefillArgs& a, const PrefillHot& h, int group,
+                                             int r, int t, int g, int split) {
   using GE = Geo<D>;
   static_assert(kRB == 1, "the wave-group merge is written for one row block per wave");
   // two LDS stages per wave group, each K + V, named statically so the
@@ -369,13 +387,14 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
   // starts at, its page id is one LDS read away, and the first tile's copy
   // waits for one memory round trip after the lengths instead of two.
   // Groups starting past kSpecTiles read the entry itself.
-  const int req_L = a.seq_lens[r];
-  const int req_o = a.q_offsets[r];
-  const int req_q0 = a.q_starts != nullptr ? a.q_starts[r] : 0;
-  const int32_t* __restrict__ ptab = a.page_table + (size_t)r * a.max_pages_per_seq;
+  const int maxp = h.max_pages_per_seq;
+  const int req_L = h.seq_lens[r];
+  const int req_o = h.q_offsets[r];
+  const int req_q0 = h.q_starts != nullptr ? h.q_starts[r] : 0;
+  const int32_t* __restrict__ ptab = h.page_table + (size_t)r * maxp;
   {
     const int lp = kPagesPerTile * lane + wave;
-    __builtin_amdgcn_global_load_lds(ptab + (lp < a.max_pages_per_seq ? lp : a.max_pages_per_seq - 1),
+    __builtin_amdgcn_global_load_lds(ptab + (lp < maxp ? lp : maxp - 1),
                                      (lds_void*)&s_spec[wave_id][0], 4, 0, 0);
   }
 
@@ -388,7 +407,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
   if (split >= nsp) return leave();
   const int kt0 = split * a.kv_tiles_per_split;
   const int kt1 = min(kt0 + a.kv_tiles_per_split, tg.ntiles);
-  const int q_start = a.q_starts != nullptr ? req_q0 : q_start_of(a, r, lane);
+  const int q_start = h.q_starts != nullptr ? req_q0 : q_start_of(a, r, lane);
 
   // this lane's query row (one 32-row block per wave)
   const int Hq = a.num_q_heads;
@@ -415,7 +434,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int group, in
 
   const __bf16* __restrict__ kpool = reinterpret_cast<const __bf16*>(a.k_pool);
   const __bf16* __restrict__ vpool = reinterpret_cast<const __bf16*>(a.v_pool);
-  const int npages = min((tg.kmax + kPageSize - 1) / kPageSize, a.max_pages_per_seq);
+  const int npages = min((tg.kmax + kPageSize - 1) / kPageSize, maxp);
 
   PageIds pi;
   pi.ptab = ptab;
