@@ -153,11 +153,15 @@ __device__ __forceinline__ int request_of_page(const int* pre, int B, int f0, bo
 // with them the compiler can prove that the kernel's own stores never touch
 // the page table, and reads page ids with scalar loads (a vector load there
 // would make each wait for a page id also wait for every K/V load in flight).
+// They and the sizes the prologue needs first lead the argument list, ahead
+// of the struct (whose fields of the same names they equal), so that the
+// library's build (kernarg preloading) hands them to the wave in SGPRs at
+// launch and the first length read waits on no load of the kernel arguments.
 template <typename T, int D, int G>
 __global__ void __launch_bounds__(kThreads)
-decode_balanced_kernel(DecodeArgs a, const int32_t* __restrict__ page_table,
-                       const int32_t* __restrict__ seq_lens, float* __restrict__ o_part,
-                       float* __restrict__ lse_part, int32_t* __restrict__ range_meta) {
+decode_balanced_kernel(const int32_t* __restrict__ seq_lens, int B, int maxp, int Hkv, int V,
+                       const int32_t* __restrict__ page_table, float* __restrict__ o_part,
+                       float* __restrict__ lse_part, int32_t* __restrict__ range_meta, DecodeArgs a) {
   using S = Shape<T, D, G>;
   // the prefetched q of the next request costs one more q register set
   using P = Pipe<T, D, G, G * S::kChunksPerLane * 4>;
@@ -171,10 +175,6 @@ decode_balanced_kernel(DecodeArgs a, const int32_t* __restrict__ page_table,
   const int col = lane % S::kLpt;
   const int row0 = lane / S::kLpt;
   const int Hq = a.num_q_heads;
-  const int Hkv = a.num_kv_heads;
-  const int B = a.num_seqs;
-  const int maxp = a.max_pages_per_seq;
-  const int V = a.num_splits;
   const int g = blockIdx.x % Hkv;
   const int v = (blockIdx.x / Hkv) * kWaves + wave;
 
@@ -610,7 +610,8 @@ hipError_t launch_bal_t(const DecodeArgs& a, hipStream_t s) {
   if (grid > 0x7FFFFFFFLL || a.num_splits % kWaves != 0 || a.num_seqs > kMaxBalancedSeqs)
     return hipErrorInvalidValue;
   hipLaunchKernelGGL((decode_balanced_kernel<T, D, G>), dim3((unsigned)grid), dim3(kThreads), 0, s,
-                     a, a.page_table, a.seq_lens, a.o_part, a.lse_part, a.range_meta);
+                     a.seq_lens, a.num_seqs, a.max_pages_per_seq, a.num_kv_heads, a.num_splits,
+                     a.page_table, a.o_part, a.lse_part, a.range_meta, a);
   return hipGetLastError();
 }
 
