@@ -96,23 +96,47 @@ __global__ void __launch_bounds__(kThreads) append_kernel(AppendArgs a) {
 // the rows it owns with (r + 1, position); the largest r wins where
 // inconsistent metadata makes two requests claim a row.  Rows past total_q
 // are never touched, so no metadata can make this kernel read past k_new.
-// The row starts, lengths, offsets and sizes come before the argument
-// struct as plain scalars and pointers (equal to the struct's fields of the
-// same names), so that the library's build preloads them into SGPRs at
-// launch and the owner scan's reads need no load of the kernel arguments.
+// The new-row sources, row starts, lengths, offsets and sizes come before
+// the argument struct as plain scalars and pointers (equal to the struct's
+// fields of the same names; row_bytes = num_kv_heads * head_bytes), so that
+// the library's build preloads them into SGPRs at launch: the owner scan's
+// reads and the group's first source loads go out without waiting on a load
+// of the kernel arguments.  The group's packed rows are contiguous in k_new
+// and v_new (chunk x of the group sits at x0 * row_bytes + 16 x), so the
+// first two chunks of each thread are requested before the metadata, on
+// which only their destination depends: the source read and the metadata
+// read share one memory round trip.  The two early chunks are loaded at a
+// clamped index (always inside the group's rows) and used only if real.
 __global__ void __launch_bounds__(kThreads)
-append_flat_kernel(const int32_t* q_starts, const int32_t* seq_lens, const int32_t* q_offsets,
-                   int num_seqs, long long total_rows, AppendArgs a) {
+append_flat_kernel(const unsigned char* __restrict__ kn, const unsigned char* __restrict__ vn,
+                   const int32_t* q_starts, const int32_t* seq_lens, const int32_t* q_offsets,
+                   int num_seqs, int row_bytes, long long total_rows, AppendArgs a) {
   __shared__ unsigned long long s_owner[kRowsPerWg];
   const int tid = threadIdx.x;
   const long long x0 = (long long)blockIdx.x * kRowsPerWg;
   const int rows = total_rows - x0 < kRowsPerWg ? (int)(total_rows - x0) : kRowsPerWg;
+  const int row_chunks = row_bytes / 16;
+  const int n_chunks = rows * row_chunks;
+  const unsigned char* __restrict__ ksrc = kn + (size_t)x0 * row_bytes;
+  const unsigned char* __restrict__ vsrc = vn + (size_t)x0 * row_bytes;
+  const int xa = tid, xb = tid + kThreads;   // this thread's first two chunks
+  const size_t oa = (size_t)(xa < n_chunks ? xa : n_chunks - 1) * 16;
+  const size_t ob = (size_t)(xb < n_chunks ? xb : n_chunks - 1) * 16;
+  const uint4 ka = *reinterpret_cast<const uint4*>(ksrc + oa);
+  const uint4 va = *reinterpret_cast<const uint4*>(vsrc + oa);
+  const uint4 kb = *reinterpret_cast<const uint4*>(ksrc + ob);
+  const uint4 vb = *reinterpret_cast<const uint4*>(vsrc + ob);
+  // this thread's request (if any), read before the barrier below
+  long long st = 0;
+  int L = 0, o = 0;
+  if (tid < num_seqs) {
+    st = q_starts[tid];
+    L = seq_lens[tid];
+    o = q_offsets[tid];
+  }
   if (tid < kRowsPerWg) s_owner[tid] = 0ull;
   __syncthreads();
   if (tid < num_seqs) {
-    const long long st = q_starts[tid];
-    const int L = seq_lens[tid];
-    const int o = q_offsets[tid];
     const int n = L - o;
     if (o >= 0 && n > 0) {
       const long long lo = st > x0 ? st : x0;
@@ -123,34 +147,38 @@ append_flat_kernel(const int32_t* q_starts, const int32_t* seq_lens, const int32
   }
   __syncthreads();
 
-  const int row_bytes = a.num_kv_heads * a.head_bytes;
-  const int row_chunks = row_bytes / 16;
   const int head_chunks = a.head_bytes / 16;
-  const unsigned char* __restrict__ kn = reinterpret_cast<const unsigned char*>(a.k_new);
-  const unsigned char* __restrict__ vn = reinterpret_cast<const unsigned char*>(a.v_new);
   unsigned char* __restrict__ kp = reinterpret_cast<unsigned char*>(a.k_pool);
   unsigned char* __restrict__ vp = reinterpret_cast<unsigned char*>(a.v_pool);
   const size_t block_bytes = (size_t)kPageSize * a.head_bytes;
-#pragma unroll 4
-  for (int x = tid; x < rows * row_chunks; x += kThreads) {
+  // chunk x of the group into its slot, if a request owns its row and the
+  // page id is inside the pool
+  auto put = [&](int x, const uint4& kv, const uint4& vv) __attribute__((always_inline)) {
     const int i = x / row_chunks;
     const int w = x % row_chunks;
     const unsigned long long own = s_owner[i];
-    if (own == 0ull) continue;   // no request owns the row
+    if (own == 0ull) return;   // no request owns the row
     const int r = (int)(own >> 32) - 1;
     const int pos = (int)(own & 0xFFFFFFFFull);
     const int pg = pos / kPageSize;
-    if (pg >= a.max_pages_per_seq) continue;
+    if (pg >= a.max_pages_per_seq) return;
     const int id = a.page_table[(size_t)r * a.max_pages_per_seq + pg];
-    if (id < 0 || id >= a.num_pages) continue;
+    if (id < 0 || id >= a.num_pages) return;
     const int h = w / head_chunks;
     const int c = w % head_chunks;
-    const size_t src = ((size_t)(x0 + i) * a.num_kv_heads + h) * a.head_bytes + (size_t)c * 16;
     const size_t dst = ((size_t)id * a.num_kv_heads + h) * block_bytes +
                        (size_t)(pos % kPageSize) * a.head_bytes + (size_t)c * 16;
-    *reinterpret_cast<uint4*>(kp + dst) = *reinterpret_cast<const uint4*>(kn + src);
-    *reinterpret_cast<uint4*>(vp + dst) = *reinterpret_cast<const uint4*>(vn + src);
-  }
+    *reinterpret_cast<uint4*>(kp + dst) = kv;
+    *reinterpret_cast<uint4*>(vp + dst) = vv;
+  };
+  if (xa < n_chunks) put(xa, ka, va);
+  if (xb < n_chunks) put(xb, kb, vb);
+  // wider rows: the rest, unrolled so that several independent page-id ->
+  // load -> store chains are in flight per thread
+#pragma unroll 4
+  for (int x = tid + 2 * kThreads; x < n_chunks; x += kThreads)
+    put(x, *reinterpret_cast<const uint4*>(ksrc + (size_t)x * 16),
+        *reinterpret_cast<const uint4*>(vsrc + (size_t)x * 16));
 }
 
 // Copy whole pages (every KV head, K and V) from src[i] to dst[i]: the device
@@ -197,8 +225,11 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
     const long long grid = (a.total_rows + kRowsPerWg - 1) / kRowsPerWg;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(append_flat_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, a.q_starts,
-                       a.seq_lens, a.q_offsets, a.num_seqs, (long long)a.total_rows, a);
+    hipLaunchKernelGGL(append_flat_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s,
+                       reinterpret_cast<const unsigned char*>(a.k_new),
+                       reinterpret_cast<const unsigned char*>(a.v_new), a.q_starts, a.seq_lens,
+                       a.q_offsets, a.num_seqs, a.num_kv_heads * a.head_bytes,
+                       (long long)a.total_rows, a);
     return hipGetLastError();
   }
   const long long grid = (long long)a.num_seqs * a.tiles_per_seq;
